@@ -1,0 +1,282 @@
+/*
+ * moe_oracle.c -- plain, slow CPU oracle for MoE token routing with
+ * equal-cost load-balancing statistics.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline leg use it.  It shares no code, header, table or constant with
+ * the HIP library.
+ *
+ * Every step is the plain definition written out in double precision, in
+ * the order the pages give it.  Pages cited (address, title, section):
+ *   [p1] mhpq.cn/news/998159, on the three layers of HPC load balancing
+ *        (LVS, NIC Teaming, MoE equal-cost balancing): section 4.2 (f_i,
+ *        P_i, aux loss), 4.4 (top-k version, f_i denominator), 4.5
+ *        (capacity), 5.3/5.4 (sanity sums, max/mean load).
+ *   [p2] codechina.net article 413310, "equal-cost load balancing in MoE
+ *        training: principles, code, tuning": section 2.2 (the aux loss and
+ *        its value 1 under uniform routing), 3.1 (histogram keeps
+ *        zero-count experts), 4.2 (distribution ratio, entropy).
+ *   [p3] cnvsn.com/news/335486, survey of load balancing for large models:
+ *        sections 3.1 and 5.1 (coefficient of variation, balance degree).
+ * Readings where the pages are silent are stated at each function.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* bf16 bit pattern -> double (exact: bf16 is the upper half of an fp32). */
+static double bf16_to_double(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float x;
+    memcpy(&x, &u, sizeof x);
+    return (double)x;
+}
+
+/*
+ * Per-microbatch expert capacity.  [p1] 4.5 sets it to the tokens-per-
+ * expert share of the batch, rounded up, times the capacity factor; its
+ * worked example is 1024 tokens, 8 experts, factor 1.25 -> 160.
+ * Reading for top-k (k assignments per token): the load to spread is Tm*k
+ * assignments, and the product with the factor is rounded up:
+ *   C = ceil(cf * ceil(Tm*k / E)).
+ * cf <= 0 means "no limit" (returned as -1).  A non-negative override wins.
+ */
+long long oracle_capacity(long long Tm, long long E, long long k, double cf,
+                          long long capacity_override)
+{
+    if (capacity_override >= 0)
+        return capacity_override;
+    if (!(cf > 0.0))
+        return -1;
+    long long per_expert = (Tm * k + E - 1) / E; /* ceil(Tm*k/E) */
+    return (long long)ceil(cf * (double)per_expert);
+}
+
+/*
+ * Gate GEMM: logits[t][e] = sum_d X[t][d] * Wg[d][e], bf16 inputs.
+ * Each bf16 product is exact in double; the sum is accumulated in double.
+ * ([p2] 1.2 names the gate/router network; the X*Wg form is the workload's.)
+ */
+void oracle_gate_logits(const uint16_t *X, const uint16_t *Wg, long long T,
+                        long long d, long long E, double *logits)
+{
+    for (long long t = 0; t < T; ++t)
+        for (long long e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (long long i = 0; i < d; ++i)
+                acc += bf16_to_double(X[t * d + i]) * bf16_to_double(Wg[i * E + e]);
+            logits[t * E + e] = acc;
+        }
+}
+
+/* Row softmax statistics: m = max_e l, s = sum_e exp(l - m). */
+static void softmax_stats(const double *row, long long E, double *m_out, double *s_out)
+{
+    double m = row[0];
+    for (long long e = 1; e < E; ++e)
+        if (row[e] > m)
+            m = row[e];
+    double s = 0.0;
+    for (long long e = 0; e < E; ++e)
+        s += exp(row[e] - m);
+    *m_out = m;
+    *s_out = s;
+}
+
+/*
+ * Top-k selection for one row: the first k experts in the order
+ * (logit descending, expert index ascending).  Comparison is numeric, so
+ * -0.0 and +0.0 are equal and the lower index wins.  Written as k passes of
+ * "take the best expert not taken yet"; a strict '>' keeps the lowest index
+ * among equal logits.
+ */
+static void topk_row(const double *row, long long E, long long k, int32_t *idx, char *taken)
+{
+    memset(taken, 0, (size_t)E);
+    for (long long j = 0; j < k; ++j) {
+        long long best = -1;
+        for (long long e = 0; e < E; ++e) {
+            if (taken[e])
+                continue;
+            if (best < 0 || row[e] > row[best])
+                best = e;
+        }
+        taken[best] = 1;
+        idx[j] = (int32_t)best;
+    }
+}
+
+/*
+ * Forward routing of T tokens split into n_micro equal microbatches of
+ * Tm = T / n_micro tokens; every microbatch is routed on its own.
+ *
+ * Outputs (all caller-allocated; pointers marked "may be NULL" are skipped):
+ *   topk_idx [T*k], topk_w [T*k]          selection and gate weights
+ *   row_max, row_sum [T]      (may be NULL) softmax statistics
+ *   counts   [m*E]             assignments per expert, before capacity
+ *   offsets  [m*(E+1)]         exclusive scan of counts, local to the
+ *                              microbatch's segment of perm
+ *   perm     [T*k]             perm[m*Tm*k + pos] = flat index t*k+j
+ *   inv_perm [T*k]  (may be NULL) inv_perm[t*k+j] = m*Tm*k + pos
+ *   dropped  [T*k]             1 if the assignment is past capacity
+ *   f, P     [m*E]             dispatch fraction and mean router probability
+ *   aux, cv, max_over_mean [m]
+ *   extra    [m*8]            min/mean, balance degree, entropy of f,
+ *                              kept, dropped, capacity, max f, min f
+ * Returns 0 on success, -1 on bad arguments.
+ */
+int oracle_route(const double *logits, long long T, long long E, long long k,
+                 long long n_micro, long long capacity, double alpha, int renorm,
+                 int32_t *topk_idx, double *topk_w, double *row_max, double *row_sum,
+                 int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm,
+                 uint8_t *dropped, double *f, double *P, double *aux, double *cv,
+                 double *max_over_mean, double *extra)
+{
+    if (T < 1 || E < 1 || k < 1 || k > E || n_micro < 1 || T % n_micro != 0)
+        return -1;
+    const long long Tm = T / n_micro;
+    char *taken = (char *)malloc((size_t)E);
+    double *psum = (double *)malloc(sizeof(double) * (size_t)E);
+    long long *cursor = (long long *)malloc(sizeof(long long) * (size_t)E);
+    if (!taken || !psum || !cursor) {
+        free(taken); free(psum); free(cursor);
+        return -1;
+    }
+
+    for (long long mb = 0; mb < n_micro; ++mb) {
+        const long long t0 = mb * Tm;
+        int32_t *cnt = counts + mb * E;
+        int32_t *off = offsets + mb * (E + 1);
+        for (long long e = 0; e < E; ++e) {
+            cnt[e] = 0;
+            psum[e] = 0.0;
+        }
+
+        /* Softmax, selection, gate weights; histogram and probability sums.
+         * [p1] 4.2: p = softmax(router(x)); f counts the argmax/top-k picks,
+         * P averages the softmax over all tokens of the batch.
+         * [p1] 4.4 / [p2] 3.1: the histogram keeps zero-count experts. */
+        for (long long t = t0; t < t0 + Tm; ++t) {
+            const double *row = logits + t * E;
+            double m, s;
+            softmax_stats(row, E, &m, &s);
+            if (row_max) row_max[t] = m;
+            if (row_sum) row_sum[t] = s;
+            for (long long e = 0; e < E; ++e)
+                psum[e] += exp(row[e] - m) / s;
+
+            int32_t *idx = topk_idx + t * k;
+            topk_row(row, E, k, idx, taken);
+            double picked = 0.0;
+            for (long long j = 0; j < k; ++j)
+                picked += exp(row[idx[j]] - m) / s;
+            for (long long j = 0; j < k; ++j) {
+                double p = exp(row[idx[j]] - m) / s;
+                /* Reading: with renorm the k picked probabilities are
+                 * rescaled to sum to one; without it the gate is p itself. */
+                topk_w[t * k + j] = renorm ? p / picked : p;
+                cnt[idx[j]] += 1;
+            }
+        }
+
+        /* Expert offsets: exclusive prefix sum of the counts. */
+        off[0] = 0;
+        for (long long e = 0; e < E; ++e)
+            off[e + 1] = off[e] + cnt[e];
+
+        /* Stable expert-sorted permutation with capacity drop.
+         * Assignments are visited in (token, slot) order; the r-th one that
+         * goes to expert e lands at off[e] + r and is dropped when r >= C.
+         * ([p1] 4.5: tokens past an expert's capacity are dropped.) */
+        for (long long e = 0; e < E; ++e)
+            cursor[e] = 0;
+        const long long seg = mb * Tm * k;
+        for (long long t = t0; t < t0 + Tm; ++t)
+            for (long long j = 0; j < k; ++j) {
+                long long a = t * k + j;
+                long long e = topk_idx[a];
+                long long r = cursor[e]++;
+                long long pos = off[e] + r;
+                perm[seg + pos] = (int32_t)a;
+                if (inv_perm) inv_perm[a] = (int32_t)(seg + pos);
+                dropped[a] = (uint8_t)(capacity >= 0 && r >= capacity);
+            }
+
+        /* Statistics.  [p1] 4.2/4.4: f_i = count_i / (Tm*k),
+         * P_i = mean softmax probability; aux = alpha * N * sum f_i * P_i.
+         * [p3] 3.1/5.1: CV = std/mean over expert loads (population std),
+         * load-balance degree = 1 - (max - mean)/mean.  [p1] 5.4: max/mean.
+         * [p2] 4.2: max and min distribution ratio; entropy of the load. */
+        const double total = (double)(Tm * k);
+        const double mean = total / (double)E;
+        double dot = 0.0, var = 0.0, ent = 0.0;
+        double cmax = cnt[0], cmin = cnt[0];
+        long long kept = 0;
+        for (long long e = 0; e < E; ++e) {
+            double fe = (double)cnt[e] / total;
+            double pe = psum[e] / (double)Tm;
+            f[mb * E + e] = fe;
+            P[mb * E + e] = pe;
+            dot += fe * pe;
+            var += ((double)cnt[e] - mean) * ((double)cnt[e] - mean);
+            if (fe > 0.0)
+                ent -= fe * log(fe);
+            if (cnt[e] > cmax) cmax = cnt[e];
+            if (cnt[e] < cmin) cmin = cnt[e];
+            kept += (capacity >= 0 && cnt[e] > capacity) ? capacity : cnt[e];
+        }
+        var /= (double)E;
+        aux[mb] = alpha * (double)E * dot;
+        cv[mb] = sqrt(var) / mean;
+        max_over_mean[mb] = cmax / mean;
+        double *x = extra + mb * 8;
+        x[0] = cmin / mean;
+        x[1] = 1.0 - (cmax - mean) / mean;
+        x[2] = ent;
+        x[3] = (double)kept;
+        x[4] = total - (double)kept;
+        x[5] = (double)capacity;
+        x[6] = cmax / total;
+        x[7] = cmin / total;
+    }
+    free(taken);
+    free(psum);
+    free(cursor);
+    return 0;
+}
+
+/*
+ * Gradient of the aux loss with respect to the logits.
+ * [p1] 4.2 and [p2] 2.2: f_i is a hard observation with no gradient; the
+ * gradient flows through P_i only.  With P_i = (1/Tm) sum_t p[t][i] and
+ * dp[t][i]/dl[t][j] = p[t][i] (delta_ij - p[t][j]):
+ *   dL/dl[t][j] = g * alpha * E / Tm * p[t][j] * (f_j - sum_i f_i p[t][i])
+ * where g is the upstream gradient of the microbatch's loss (1 if NULL).
+ */
+void oracle_backward(const double *logits, long long T, long long E, long long k,
+                     long long n_micro, double alpha, const int32_t *counts,
+                     const double *d_aux, double *dlogits)
+{
+    const long long Tm = T / n_micro;
+    for (long long mb = 0; mb < n_micro; ++mb) {
+        const double g = d_aux ? d_aux[mb] : 1.0;
+        const double c = g * alpha * (double)E / (double)Tm;
+        const int32_t *cnt = counts + mb * E;
+        for (long long t = mb * Tm; t < (mb + 1) * Tm; ++t) {
+            const double *row = logits + t * E;
+            double m, s;
+            softmax_stats(row, E, &m, &s);
+            double dotfp = 0.0;
+            for (long long i = 0; i < E; ++i)
+                dotfp += ((double)cnt[i] / (double)(Tm * k)) * (exp(row[i] - m) / s);
+            for (long long j = 0; j < E; ++j) {
+                double p = exp(row[j] - m) / s;
+                double fj = (double)cnt[j] / (double)(Tm * k);
+                dlogits[t * E + j] = c * p * (fj - dotfp);
+            }
+        }
+    }
+}

@@ -1,0 +1,106 @@
+"""ctypes front end of the C oracle (``moe_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY.  Arrays in and out are numpy; all floating point is
+float64.  See ``moe_oracle.c`` for the definitions and the page citations.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+_lib = None
+
+
+def load_library(path=None):
+    """Load (building first if needed) the oracle library; cached."""
+    global _lib
+    if path is None and _lib is not None:
+        return _lib
+    p = path or _build.LIB
+    if not os.path.exists(p):
+        _build.build(out=p)
+    lib = ctypes.CDLL(p)
+    ll, d, vp, i = ctypes.c_longlong, ctypes.c_double, ctypes.c_void_p, ctypes.c_int
+    lib.oracle_capacity.argtypes = [ll, ll, ll, d, ll]
+    lib.oracle_capacity.restype = ll
+    lib.oracle_gate_logits.argtypes = [vp, vp, ll, ll, ll, vp]
+    lib.oracle_gate_logits.restype = None
+    lib.oracle_route.argtypes = [vp, ll, ll, ll, ll, ll, d, i] + [vp] * 15
+    lib.oracle_route.restype = i
+    lib.oracle_backward.argtypes = [vp, ll, ll, ll, ll, d, vp, vp, vp]
+    lib.oracle_backward.restype = None
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def capacity(Tm, E, k, capacity_factor, capacity_override=-1, lib=None):
+    """Per-microbatch capacity C (``-1`` = unlimited)."""
+    lib = lib or load_library()
+    return int(lib.oracle_capacity(int(Tm), int(E), int(k), float(capacity_factor),
+                                   int(capacity_override)))
+
+
+def gate_logits(X_bits, Wg_bits, lib=None):
+    """fp64 logits of X[T,d] @ Wg[d,E] from bf16 bit patterns (uint16 arrays)."""
+    lib = lib or load_library()
+    X = np.ascontiguousarray(X_bits, dtype=np.uint16)
+    W = np.ascontiguousarray(Wg_bits, dtype=np.uint16)
+    T, d = X.shape
+    d2, E = W.shape
+    assert d == d2
+    out = np.empty((T, E), np.float64)
+    lib.oracle_gate_logits(_p(X), _p(W), T, d, E, _p(out))
+    return out
+
+
+def route(logits, k, n_micro=1, capacity_factor=1.0, capacity_override=-1,
+          alpha=0.01, renorm=False, lib=None):
+    """Route ``logits`` [T,E] (any float dtype; widened exactly to float64).
+
+    Returns a dict of numpy arrays named like the C-ABI outputs, plus
+    ``capacity`` (int, -1 = unlimited).
+    """
+    lib = lib or load_library()
+    L = np.ascontiguousarray(logits, dtype=np.float64)
+    T, E = L.shape
+    m = int(n_micro)
+    if T % m:
+        raise ValueError("T must be a multiple of n_micro")
+    C = capacity(T // m, E, k, capacity_factor, capacity_override, lib=lib)
+    o = dict(
+        topk_idx=np.empty((T, k), np.int32), topk_w=np.empty((T, k), np.float64),
+        row_max=np.empty(T, np.float64), row_sum=np.empty(T, np.float64),
+        counts=np.empty((m, E), np.int32), offsets=np.empty((m, E + 1), np.int32),
+        perm=np.empty(T * k, np.int32), inv_perm=np.empty(T * k, np.int32),
+        dropped=np.empty(T * k, np.uint8), f=np.empty((m, E), np.float64),
+        P=np.empty((m, E), np.float64), aux=np.empty(m, np.float64),
+        cv=np.empty(m, np.float64), max_over_mean=np.empty(m, np.float64),
+        extra=np.empty((m, 8), np.float64))
+    rc = lib.oracle_route(_p(L), T, E, int(k), m, C, float(alpha), int(bool(renorm)),
+                          *[_p(o[n]) for n in ("topk_idx", "topk_w", "row_max", "row_sum",
+                                               "counts", "offsets", "perm", "inv_perm",
+                                               "dropped", "f", "P", "aux", "cv",
+                                               "max_over_mean", "extra")])
+    if rc != 0:
+        raise ValueError("oracle_route rejected its arguments")
+    o["capacity"] = C
+    return o
+
+
+def backward(logits, k, counts, n_micro=1, alpha=0.01, d_aux=None, lib=None):
+    """dL_aux/dlogits [T,E] (float64) given the forward's pre-capacity counts."""
+    lib = lib or load_library()
+    L = np.ascontiguousarray(logits, dtype=np.float64)
+    T, E = L.shape
+    cnt = np.ascontiguousarray(counts, dtype=np.int32).reshape(n_micro, E)
+    g = None if d_aux is None else np.ascontiguousarray(d_aux, dtype=np.float64).reshape(n_micro)
+    out = np.empty((T, E), np.float64)
+    lib.oracle_backward(_p(L), T, E, int(k), int(n_micro), float(alpha), _p(cnt), _p(g), _p(out))
+    return out

@@ -1,0 +1,385 @@
+"""Pins of the CPU oracle to facts fixed by the pages and by mathematics.
+
+Each ``pin_*`` function takes an oracle library handle (``oracle.load_library``)
+so that ``test_oracle_pins.py`` runs them on the real oracle and
+``test_oracle_mutants.py`` runs them on copies with planted mistakes.
+
+Pages (address, subject, section):
+  [p1] mhpq.cn/news/998159 -- three layers of HPC load balancing; MoE part:
+       4.2 (f_i, P_i, aux loss), 4.4 (top-k: f over T*k), 4.5 (capacity and
+       its worked example), 5.3 (f and P each sum to one), 5.4 (max/mean).
+  [p2] codechina.net article 413310 -- equal-cost balancing in MoE training:
+       2.2 (uniform routing gives a normalised loss of 1; two hot experts
+       raise it; gradient only through P), 3.1 (histogram with minlength),
+       4.2 (max/min distribution ratio, entropy of the load).
+  [p3] cnvsn.com/news/335486 -- load-balancing survey: 3.1/5.1 (CV = std/mean,
+       balance degree 1 - (max-mean)/mean).
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            for tok in line.split():
+                key, val = tok.split("=")
+                vals[key] = float(val)
+    return vals
+
+
+def _route(lib, L, k, **kw):
+    return oracle.route(L, k, lib=lib, **kw)
+
+
+# ----------------------------------------------------------------- capacity
+def pin_capacity_worked_example(lib):
+    """[p1] 4.5: 1024 tokens, 8 experts, factor 1.25 -> 160 per expert; the
+    overflow beyond 160 of each expert is dropped."""
+    g = _golden("capacity_worked_example.txt")
+    T, E, k = int(g["tokens"]), int(g["experts"]), int(g["top_k"])
+    C = oracle.capacity(T, E, k, g["capacity_factor"], lib=lib)
+    assert C == int(g["capacity"])
+    # The same formula where tokens do not divide evenly: for top-1 and an
+    # integral product it is ceil(tokens / experts) * factor exactly.
+    for toks, ne, cf, want in [(1001, 8, 1.0, 126), (1000, 7, 2.0, 286), (9, 4, 3.0, 9)]:
+        assert oracle.capacity(toks, ne, 1, cf, lib=lib) == want
+    rng = np.random.default_rng(11)
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    L[:, 0] += 1.5  # expert 0 overloaded
+    o = _route(lib, L, k, capacity_factor=g["capacity_factor"], alpha=0.01, renorm=False)
+    counts = o["counts"][0]
+    dropped_per_e = np.bincount(o["topk_idx"].ravel(), weights=o["dropped"], minlength=E)
+    assert counts[0] > C
+    assert np.array_equal(dropped_per_e.astype(np.int64), np.maximum(counts - C, 0))
+
+
+def pin_balanced_routing_drops_nothing(lib):
+    """[p1] 4.5 recommends factors near 1.0 for peak efficiency, which only
+    makes sense if perfectly balanced routing at factor 1.0 drops nothing.
+    Holds for every k (fails if the capacity ignored the k picks per token)."""
+    for E, k in [(8, 1), (8, 2), (16, 4), (12, 3)]:
+        Tm = 4 * E
+        base = np.linspace(2.0, -2.0, E)
+        L = np.stack([np.roll(base, t % E) for t in range(Tm)]).astype(np.float32)
+        o = _route(lib, L, k, capacity_factor=1.0, alpha=0.01)
+        assert o["dropped"].sum() == 0, (E, k)
+        # and factor 0.5 drops exactly half of every expert's (equal) load
+        o = _route(lib, L, k, capacity_factor=0.5, alpha=0.01)
+        assert o["dropped"].sum() == Tm * k // 2, (E, k)
+
+
+# ------------------------------------------------------- loss closed forms
+def pin_uniform_logits_loss_is_alpha(lib):
+    """[p2] 2.2: f = P = 1/N gives N*sum f*P = 1.  With equal logits the
+    softmax is exactly 1/E, so sum f*P = 1/E whatever the (tied) picks are,
+    and the aux loss is alpha for every k.  Ties go to the lowest index."""
+    g = _golden("uniform_routing_loss.txt")
+    for E, k, alpha, c in [(8, 1, 0.01, 0.0), (8, 2, 0.5, 3.25), (64, 2, 0.01, -1.0),
+                           (6, 6, 1.0, 0.0), (5, 3, 0.25, 7.0)]:
+        T = 20
+        L = np.full((T, E), c, np.float32)
+        o = _route(lib, L, k, capacity_factor=1.25, alpha=alpha)
+        assert np.allclose(o["P"], 1.0 / E, rtol=0, atol=1e-15)
+        assert abs(o["aux"][0] / alpha - g["normalized_loss_uniform"]) < 1e-12
+        assert np.array_equal(o["topk_idx"], np.tile(np.arange(k), (T, 1)))
+
+
+def pin_cyclic_logits_perfect_balance(lib):
+    """Rows that are rotations of one vector, Tm a multiple of E: every expert
+    gets Tm*k/E picks and P = 1/E, so f = P = 1/N and the normalised loss is
+    1 ([p2] 2.2), CV = 0 and max/mean = 1 ([p3] 3.1, [p1] 5.4), balance
+    degree 1, entropy ln E."""
+    for E, k, m in [(8, 1, 1), (8, 2, 2), (16, 5, 1), (7, 3, 3)]:
+        Tm = 3 * E
+        rng = np.random.default_rng(E * 100 + k)
+        base = rng.standard_normal(E)
+        rows = [np.roll(base, t % E) for t in range(Tm)]
+        L = np.concatenate([np.stack(rows)] * m).astype(np.float32)
+        alpha = 0.03
+        o = _route(lib, L, k, n_micro=m, capacity_factor=2.0, alpha=alpha)
+        for mb in range(m):
+            assert np.all(o["counts"][mb] == Tm * k // E)
+            assert np.allclose(o["f"][mb], 1.0 / E, atol=1e-15)
+            assert np.allclose(o["P"][mb], 1.0 / E, atol=1e-14)
+            assert abs(o["aux"][mb] - alpha) < 1e-14
+            assert abs(o["cv"][mb]) < 1e-14
+            assert abs(o["max_over_mean"][mb] - 1.0) < 1e-14
+            ex = o["extra"][mb]
+            assert abs(ex[0] - 1.0) < 1e-14 and abs(ex[1] - 1.0) < 1e-14
+            assert abs(ex[2] - math.log(E)) < 1e-12
+
+
+def pin_two_hot_experts_raise_loss(lib):
+    """[p2] 2.2: when two experts take most of the tokens the loss exceeds the
+    uniform value; it grows with the imbalance."""
+    rng = np.random.default_rng(5)
+    T, E = 512, 8
+    prev = None
+    for boost in [0.0, 1.0, 2.0, 4.0]:
+        L = rng.standard_normal((T, E)).astype(np.float32)
+        L[:, :2] += boost
+        o = _route(lib, L, 1, capacity_factor=1.0, alpha=1.0)
+        if boost >= 2.0:
+            assert o["counts"][0, :2].sum() > 0.8 * T
+            assert o["aux"][0] > 2.0
+        if prev is not None:
+            assert o["aux"][0] > prev
+        prev = o["aux"][0]
+
+
+def pin_sums_are_one(lib):
+    """[p1] 5.3: f and P each sum to 1 (catches a missing division by k);
+    [p1] 4.4: the counts sum to Tm*k assignments."""
+    rng = np.random.default_rng(3)
+    for E, k, m in [(8, 1, 1), (64, 2, 2), (32, 7, 4), (5, 5, 1)]:
+        Tm = 40
+        L = np.round(rng.standard_normal((Tm * m, E)), 1).astype(np.float32)  # ties
+        o = _route(lib, L, k, n_micro=m, capacity_factor=1.0, alpha=0.01)
+        for mb in range(m):
+            assert o["counts"][mb].sum() == Tm * k
+            assert abs(o["f"][mb].sum() - 1.0) < 1e-13
+            assert abs(o["P"][mb].sum() - 1.0) < 1e-13
+
+
+# ------------------------------------------------------------------ top-k
+def _sorted_order_bruteforce(row):
+    """The unique permutation sorted by (value desc, index asc), found by
+    trying every permutation (tiny E only)."""
+    E = len(row)
+    for perm in itertools.permutations(range(E)):
+        ok = True
+        for a, b in zip(perm, perm[1:]):
+            if not (row[a] > row[b] or (row[a] == row[b] and a < b)):
+                ok = False
+                break
+        if ok:
+            return list(perm)
+    raise AssertionError("no sorted permutation")
+
+
+def pin_topk_bruteforce_ties(lib):
+    """Every row over {-1, -0.0, +0.0, 1}^E for E <= 4 (and random rows for
+    E = 5, 6): selection equals the first k of the brute-force sorted order,
+    with -0.0 == +0.0 and ties to the lower expert index."""
+    vals = [-1.0, -0.0, 0.0, 1.0]
+    for E in [1, 2, 3, 4]:
+        rows = np.array(list(itertools.product(vals, repeat=E)), np.float32)
+        expect = [_sorted_order_bruteforce(r) for r in rows]
+        for k in range(1, E + 1):
+            o = _route(lib, rows, k, capacity_factor=0.0, alpha=0.01)
+            got = o["topk_idx"]
+            for i in range(len(rows)):
+                assert list(got[i]) == expect[i][:k], (rows[i], k)
+    rng = np.random.default_rng(7)
+    for E in [5, 6]:
+        rows = rng.integers(-2, 3, size=(60, E)).astype(np.float32)
+        expect = [_sorted_order_bruteforce(r) for r in rows]
+        for k in [1, 2, E - 1]:
+            o = _route(lib, rows, k, capacity_factor=0.0, alpha=0.01)
+            for i in range(len(rows)):
+                assert list(o["topk_idx"][i]) == expect[i][:k]
+
+
+def pin_topk_vs_lexsort(lib):
+    """np.lexsort (a textbook stable sort) on (index asc within value desc)."""
+    rng = np.random.default_rng(8)
+    for E, k in [(64, 2), (256, 8), (384, 6), (33, 16)]:
+        L = np.round(rng.standard_normal((200, E)) * 4) / 4  # many ties
+        L = L.astype(np.float32)
+        o = _route(lib, L, k, capacity_factor=0.0, alpha=0.01)
+        for i in range(L.shape[0]):
+            order = np.lexsort((np.arange(E), -L[i].astype(np.float64)))
+            assert np.array_equal(o["topk_idx"][i], order[:k])
+
+
+# --------------------------------------------------------- softmax, weights
+def pin_softmax_vs_library(lib):
+    """With k = E and no renorm the weights are the full softmax in selection
+    order: compare with torch.softmax in float64 (a library routine), and for
+    E = 2 with the logistic function 1/(1+exp(-(l0-l1)))."""
+    import torch
+    rng = np.random.default_rng(9)
+    for E in [2, 5, 16]:
+        L = (rng.standard_normal((50, E)) * 3).astype(np.float32)
+        o = _route(lib, L, E, capacity_factor=0.0, alpha=0.01, renorm=False)
+        p = torch.softmax(torch.from_numpy(L.astype(np.float64)), dim=-1).numpy()
+        p_sel = np.take_along_axis(p, o["topk_idx"].astype(np.int64), axis=1)
+        assert np.allclose(o["topk_w"], p_sel, rtol=1e-14, atol=1e-300)
+        if E == 2:
+            l = L.astype(np.float64)
+            p0 = 1.0 / (1.0 + np.exp(-(l[:, 0] - l[:, 1])))
+            w0 = np.where(o["topk_idx"][:, 0] == 0, o["topk_w"][:, 0], o["topk_w"][:, 1])
+            assert np.allclose(w0, p0, rtol=1e-14)
+
+
+def pin_weights_renorm(lib):
+    """Renormalised top-1 weight is exactly 1; renormalised top-E weights are
+    the softmax itself; renormalised top-k weights sum to 1."""
+    rng = np.random.default_rng(10)
+    L = rng.standard_normal((30, 8)).astype(np.float32)
+    o = _route(lib, L, 1, capacity_factor=0.0, renorm=True)
+    assert np.all(o["topk_w"] == 1.0)
+    o_full = _route(lib, L, 8, capacity_factor=0.0, renorm=True)
+    o_raw = _route(lib, L, 8, capacity_factor=0.0, renorm=False)
+    assert np.allclose(o_full["topk_w"], o_raw["topk_w"], rtol=1e-14)
+    o3 = _route(lib, L, 3, capacity_factor=0.0, renorm=True)
+    assert np.allclose(o3["topk_w"].sum(1), 1.0, rtol=1e-14)
+    o3r = _route(lib, L, 3, capacity_factor=0.0, renorm=False)
+    assert np.allclose(o3["topk_w"], o3r["topk_w"] / o3r["topk_w"].sum(1, keepdims=True),
+                       rtol=1e-14)
+
+
+# ------------------------------------------------- histogram, scan, scatter
+def pin_counts_offsets_perm(lib):
+    """[p2] 3.1: counts = bincount(minlength=E) (zero-count experts kept);
+    offsets = exclusive prefix sum; perm = a stable argsort of the expert ids
+    per microbatch (textbook); inv_perm inverts perm; the dropped
+    assignments of each expert are the tail past capacity."""
+    rng = np.random.default_rng(12)
+    for E, k, m, cf in [(64, 2, 1, 1.0), (16, 3, 4, 1.0), (8, 1, 2, 0.5), (40, 4, 3, 0.0)]:
+        Tm = 96
+        L = rng.standard_normal((Tm * m, E)).astype(np.float32)
+        L[:, : E // 4] += 1.0
+        o = _route(lib, L, k, n_micro=m, capacity_factor=cf, alpha=0.01)
+        C = o["capacity"]
+        idx = o["topk_idx"].reshape(m, Tm * k)
+        for mb in range(m):
+            cnt = np.bincount(idx[mb], minlength=E)
+            assert np.array_equal(o["counts"][mb], cnt)
+            assert np.array_equal(o["offsets"][mb], np.concatenate([[0], np.cumsum(cnt)]))
+            seg = o["perm"][mb * Tm * k:(mb + 1) * Tm * k]
+            expect = np.argsort(idx[mb], kind="stable") + mb * Tm * k
+            assert np.array_equal(seg, expect)
+            for e in range(E):
+                a = seg[o["offsets"][mb][e]:o["offsets"][mb][e + 1]]
+                d = o["dropped"][a]
+                keep = cnt[e] if C < 0 else min(cnt[e], C)
+                assert np.all(d[:keep] == 0) and np.all(d[keep:] == 1)
+        assert np.array_equal(o["inv_perm"][o["perm"]], np.arange(Tm * m * k))
+
+
+def pin_microbatches_independent(lib):
+    """Each microbatch is routed on its own: routing m microbatches at once
+    equals routing each one alone (perm shifted by the segment start)."""
+    rng = np.random.default_rng(13)
+    E, k, m, Tm = 24, 3, 4, 50
+    L = rng.standard_normal((Tm * m, E)).astype(np.float32)
+    o = _route(lib, L, k, n_micro=m, capacity_factor=1.0, alpha=0.02)
+    for mb in range(m):
+        s = _route(lib, L[mb * Tm:(mb + 1) * Tm], k, capacity_factor=1.0, alpha=0.02)
+        assert np.array_equal(o["counts"][mb], s["counts"][0])
+        assert np.array_equal(o["perm"][mb * Tm * k:(mb + 1) * Tm * k] - mb * Tm * k, s["perm"])
+        assert np.array_equal(o["dropped"][mb * Tm * k:(mb + 1) * Tm * k], s["dropped"])
+        assert o["aux"][mb] == s["aux"][0]
+
+
+# -------------------------------------------------------------- statistics
+def pin_stats_vs_numpy(lib):
+    """[p3] 3.1/5.1: CV = population std / mean (np.std, ddof=0) and balance
+    degree; [p1] 5.4: max/mean; [p2] 4.2: max/min distribution ratio and the
+    entropy of the load (scipy.stats.entropy, natural log)."""
+    from scipy.stats import entropy
+    rng = np.random.default_rng(14)
+    for E, k, cf in [(64, 2, 1.0), (8, 1, 1.25), (256, 8, 1.25), (10, 3, 0.0)]:
+        Tm = 300
+        L = rng.standard_normal((Tm, E)).astype(np.float32) - np.log(np.arange(1, E + 1))
+        o = _route(lib, L, k, capacity_factor=cf, alpha=0.01)
+        c = o["counts"][0].astype(np.float64)
+        mean = Tm * k / E
+        assert abs(o["cv"][0] - np.std(c) / mean) < 1e-12
+        assert abs(o["max_over_mean"][0] - c.max() / mean) < 1e-12
+        ex = o["extra"][0]
+        assert abs(ex[0] - c.min() / mean) < 1e-12
+        assert abs(ex[1] - (1 - (c.max() - mean) / mean)) < 1e-12
+        assert abs(ex[2] - entropy(c / c.sum())) < 1e-12
+        C = o["capacity"]
+        kept = c.sum() if C < 0 else np.minimum(c, C).sum()
+        assert ex[3] == kept and ex[4] == Tm * k - kept and ex[5] == C
+        assert ex[6] == c.max() / c.sum() and ex[7] == c.min() / c.sum()
+        assert ex[4] == o["dropped"].sum()
+
+
+# ---------------------------------------------------------------- backward
+def pin_backward_finite_differences(lib):
+    """[p1] 4.2 / [p2] 2.2: the gradient flows through P only (f is an
+    observation).  Central differences of the oracle's own forward aux loss
+    (f unchanged by the tiny steps) match the backward."""
+    rng = np.random.default_rng(15)
+    for E, k, m in [(5, 2, 1), (8, 1, 2), (6, 3, 1)]:
+        Tm = 7
+        L = rng.standard_normal((Tm * m, E))
+        alpha = 0.37
+        g = rng.standard_normal(m)
+        o = _route(lib, L, k, n_micro=m, capacity_factor=0.0, alpha=alpha)
+        grad = oracle.backward(L, k, o["counts"], n_micro=m, alpha=alpha, d_aux=g, lib=lib)
+        h = 1e-6
+        fd = np.zeros_like(L)
+        for t in range(L.shape[0]):
+            for e in range(E):
+                Lp = L.copy(); Lp[t, e] += h
+                Lm = L.copy(); Lm[t, e] -= h
+                op = _route(lib, Lp, k, n_micro=m, capacity_factor=0.0, alpha=alpha)
+                om = _route(lib, Lm, k, n_micro=m, capacity_factor=0.0, alpha=alpha)
+                assert np.array_equal(op["counts"], o["counts"])
+                assert np.array_equal(om["counts"], o["counts"])
+                fd[t, e] = np.dot(g, (op["aux"] - om["aux"])) / (2 * h)
+        assert np.allclose(grad, fd, rtol=1e-6, atol=1e-9)
+
+
+def pin_backward_autograd(lib):
+    """torch.autograd (float64) of the loss with f detached equals the
+    backward; the gradient of each row sums to zero; alpha = 0 or perfectly
+    balanced f (all 1/E) give a zero gradient."""
+    import torch
+    rng = np.random.default_rng(16)
+    E, k, m, Tm = 12, 3, 2, 20
+    L = rng.standard_normal((Tm * m, E))
+    alpha = 0.05
+    o = _route(lib, L, k, n_micro=m, capacity_factor=0.0, alpha=alpha)
+    g = np.array([1.0, -2.5])
+    grad = oracle.backward(L, k, o["counts"], n_micro=m, alpha=alpha, d_aux=g, lib=lib)
+    Lt = torch.tensor(L, requires_grad=True)
+    f = torch.tensor(o["counts"] / (Tm * k))
+    p = torch.softmax(Lt, dim=-1).reshape(m, Tm, E)
+    loss = (torch.tensor(g) * alpha * E * (f * p.mean(dim=1)).sum(dim=1)).sum()
+    loss.backward()
+    assert np.allclose(grad, Lt.grad.numpy(), rtol=1e-12, atol=1e-15)
+    assert np.allclose(grad.sum(axis=1), 0.0, atol=1e-15)
+    z = oracle.backward(L, k, o["counts"], n_micro=m, alpha=0.0, lib=lib)
+    assert np.all(z == 0.0)
+    E2, k2, Tm2 = 8, 2, 16
+    L2 = rng.standard_normal((Tm2, E2))
+    bal = np.full((1, E2), Tm2 * k2 // E2, np.int32)
+    z2 = oracle.backward(L2, k2, bal, n_micro=1, alpha=0.3, lib=lib)
+    assert np.allclose(z2, 0.0, atol=1e-17)
+
+
+# ---------------------------------------------------------------- gate GEMM
+def pin_gate_logits_vs_matmul(lib):
+    """The gate logits equal torch.matmul in float64 of the widened bf16
+    inputs (a library routine), and each logit is the exact dot product."""
+    import torch
+    from load_balancing_statistics_amd.workloads import f32_to_bf16_bits, bf16_bits_to_f32
+    rng = np.random.default_rng(17)
+    T, d, E = 37, 96, 5
+    X = f32_to_bf16_bits(rng.standard_normal((T, d), dtype=np.float32))
+    W = f32_to_bf16_bits(0.02 * rng.standard_normal((d, E), dtype=np.float32))
+    got = oracle.gate_logits(X, W, lib=lib)
+    ref = torch.matmul(torch.from_numpy(bf16_bits_to_f32(X).astype(np.float64)),
+                       torch.from_numpy(bf16_bits_to_f32(W).astype(np.float64))).numpy()
+    assert np.allclose(got, ref, rtol=1e-13, atol=1e-15)
+
+
+ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

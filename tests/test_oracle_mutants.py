@@ -1,0 +1,94 @@
+"""The pins are strong enough: every planted mistake in the oracle fails one.
+
+Each mutant is a copy of ``oracle/moe_oracle.c`` with one plausible mistake
+(a dropped term, a wrong sign, index or operand), compiled with gcc into a
+temporary directory.  The test passes when at least one pin rejects it.
+CPU only; the real oracle source is never modified.
+"""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+from oracle import build as obuild
+
+SRC = obuild.SRC
+
+MUTANTS = {
+    "f_over_T_not_Tk": ("double fe = (double)cnt[e] / total;",
+                        "double fe = (double)cnt[e] / (double)Tm;"),
+    "P_missing_normaliser": ("psum[e] += exp(row[e] - m) / s;",
+                             "psum[e] += exp(row[e] - m);"),
+    "P_masked_to_picks": ("psum[e] += exp(row[e] - m) / s;",
+                          "psum[e] += 0.0;"),
+    "tie_to_higher_index": ("if (best < 0 || row[e] > row[best])",
+                            "if (best < 0 || row[e] >= row[best])"),
+    "aux_missing_alpha": ("aux[mb] = alpha * (double)E * dot;",
+                          "aux[mb] = (double)E * dot;"),
+    "aux_missing_N": ("aux[mb] = alpha * (double)E * dot;",
+                      "aux[mb] = alpha * dot;"),
+    "capacity_ignores_k": ("long long per_expert = (Tm * k + E - 1) / E;",
+                           "long long per_expert = (Tm + E - 1) / E;"),
+    "capacity_floor": ("long long per_expert = (Tm * k + E - 1) / E;",
+                       "long long per_expert = (Tm * k) / E + (Tm * k) % 2;"),
+    "drop_off_by_one": ("dropped[a] = (uint8_t)(capacity >= 0 && r >= capacity);",
+                        "dropped[a] = (uint8_t)(capacity >= 0 && r > capacity);"),
+    "perm_reversed_in_expert": ("long long pos = off[e] + r;",
+                                "long long pos = off[e + 1] - 1 - r;"),
+    "offsets_inclusive": ("off[e + 1] = off[e] + cnt[e];",
+                          "off[e + 1] = off[e] + cnt[e] + (e == 0);"),
+    "cv_sample_std": ("var /= (double)E;", "var /= (double)(E - 1);"),
+    "renorm_ignored": ("topk_w[t * k + j] = renorm ? p / picked : p;",
+                       "topk_w[t * k + j] = p;"),
+    "grad_sign": ("dlogits[t * E + j] = c * p * (fj - dotfp);",
+                  "dlogits[t * E + j] = c * p * (dotfp - fj);"),
+    "grad_missing_p": ("dlogits[t * E + j] = c * p * (fj - dotfp);",
+                       "dlogits[t * E + j] = c * (fj - dotfp);"),
+    "grad_missing_E": ("const double c = g * alpha * (double)E / (double)Tm;",
+                       "const double c = g * alpha / (double)Tm;"),
+    "gate_transposed_Wg": ("bf16_to_double(Wg[i * E + e])",
+                           "bf16_to_double(Wg[(e * d + i) % (d * E)])"),
+    "entropy_log2": ("ent -= fe * log(fe);", "ent -= fe * log2(fe);"),
+    "balance_degree_sign": ("x[1] = 1.0 - (cmax - mean) / mean;",
+                            "x[1] = 1.0 + (cmax - mean) / mean;"),
+}
+
+
+_RUNNER = r"""
+import json, sys
+sys.path[:0] = [sys.argv[1], sys.argv[2]]
+import oracle
+lib = oracle.load_library(sys.argv[3])
+failed = []
+for pin in ALL_PINS:
+    try:
+        pin(lib)
+    except AssertionError:
+        failed.append(pin.__name__)
+print(json.dumps(failed))
+"""
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_reject_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    with open(SRC) as fh:
+        src = fh.read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique/found"
+    csrc = os.path.join(tmp_path, "mutant.c")
+    with open(csrc, "w") as fh:
+        fh.write(src.replace(old, new))
+    so = obuild.build(src=csrc, out=os.path.join(tmp_path, "libmutant.so"))
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    tests = os.path.join(root, "tests")
+    # A subprocess, so that a mutant that writes out of bounds and crashes
+    # counts as caught instead of taking the test runner down.
+    r = subprocess.run([sys.executable, "-c", _RUNNER, root, tests, so],
+                       capture_output=True, text=True, timeout=600)
+    if r.returncode != 0:
+        return  # crashed or raised: the mutant is caught
+    failed = json.loads(r.stdout.strip().splitlines()[-1])
+    assert failed, f"no pin rejects mutant {name}"
