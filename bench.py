@@ -1,0 +1,272 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE routing hot path on one MI355X.
+
+One step = one pass of the whole routing path over one batch of synthetic
+router logits: softmax, top-k, expert histogram, f/P, aux loss, expert
+offsets, stable capacity-limited dispatch permutation and the imbalance
+statistics (plus the gate GEMM and/or the aux-loss backward for workloads
+that include them).  Inputs are resident in HBM before timing starts and are
+rotated over several copies (> 512 MB in total) so that the 256 MB Infinity
+Cache cannot serve them.  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3_shape]
+"""
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed tokens/sec at 1 GPU + achieved HBM GB/s vs peak (E=256 top-8, T=131072)"
+HBM_PEAK_GBPS = 8000.0
+ROTATE_BYTES = 600 * 1024 * 1024
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="v3_shape")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU work budget of the oracle baseline (0 disables it)")
+    return ap.parse_args()
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime PyTorch loaded (plumbing)."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so.7")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        h = ctypes.c_void_p()
+        if self.lib.hipEventCreate(ctypes.byref(h)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return h.value
+
+    def record(self, ev, stream):
+        if self.lib.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, ev):
+        self.lib.hipEventDestroy(ctypes.c_void_p(ev))
+
+
+def alg_bytes(w, T):
+    """Algorithmic bytes of one step: only what the method must move (no
+    workspace partials, no re-reads).  Per logit 4 B read; per assignment 8 B
+    (index + weight) from the row pass and 5 B (perm + drop flag) from the
+    scatter; per token 8 B of softmax statistics when the backward follows;
+    gate path: X and Wg read, fp32 logits written; backward: logits and
+    statistics read, gradient written."""
+    k, E, d = w.k, w.E, w.d
+    stats = 8 * T if w.backward else 0
+    rows = 4 * T * E + 8 * T * k + stats
+    gate = (2 * T * d + 2 * d * E + 4 * T * E) if d > 0 else 0
+    scatter = 5 * T * k
+    bwd = (8 * T * E + 8 * T) if w.backward else 0
+    forward = (gate + 8 * T * k + stats + scatter) if d > 0 else (rows + scatter)
+    return {"rows": rows, "gate": gate, "scatter": scatter, "backward": bwd, "forward": forward}
+
+
+def cpu_baseline(w, inp, budget_s):
+    import numpy as np
+    import oracle
+    L = inp["logits"] if "logits" in inp else None
+    if L is None:
+        X, Wg = inp["X"], inp["Wg"]
+    T = w.T
+    # rate on a small prefix, then a prefix sized for the budget
+    n0 = min(T, max(w.n_micro, 2048 // max(1, w.n_micro) * w.n_micro))
+
+    def run(n):
+        t0 = time.perf_counter()
+        m = w.n_micro if n % w.n_micro == 0 and n == T else 1
+        if L is not None:
+            lg = L[:n]
+        else:
+            lg = oracle.gate_logits(X[:n], Wg)
+        o = oracle.route(lg, w.k, n_micro=m, capacity_factor=w.capacity_factor, alpha=w.alpha,
+                         renorm=w.renorm)
+        if w.backward:
+            oracle.backward(lg, w.k, o["counts"], n_micro=m, alpha=w.alpha)
+        return time.perf_counter() - t0
+
+    t_small = run(n0)
+    n = int(min(T, max(n0, n0 * budget_s / max(t_small, 1e-6))))
+    reps, tokens, elapsed = 0, 0, 0.0
+    while elapsed < budget_s * 0.5 or reps == 0:
+        elapsed += run(n)
+        tokens += n
+        reps += 1
+        if reps >= 64:
+            break
+    sample = (f"oracle (serial C, fp64) on the first {n} tokens of the seed-0 {w.name} inputs"
+              f" x{reps} pass(es): forward" + (" + backward" if w.backward else "")
+              + (" incl. gate GEMM" if w.d > 0 else ""))
+    return {"value": tokens / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": sample, "seconds": round(elapsed, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import load_balancing_statistics_amd as lbs
+    from load_balancing_statistics_amd.workloads import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = make_inputs(w, 0)
+    p = lbs.make_params(w.T, w.E, w.k, n_micro=w.n_micro, d=w.d,
+                        capacity_factor=w.capacity_factor, alpha=w.alpha, renorm=w.renorm,
+                        save_row_stats=w.backward)
+    # input copies for cache rotation
+    if w.d > 0:
+        X0 = torch.from_numpy(inp["X"].view(np.int16)).to(dev)
+        Wg = torch.from_numpy(inp["Wg"].view(np.int16)).to(dev)
+        per_copy = X0.numel() * 2
+        ncopy = max(1, math.ceil(ROTATE_BYTES / per_copy))
+        srcs = [X0] + [X0.clone() for _ in range(ncopy - 1)]
+    else:
+        L0 = torch.from_numpy(inp["logits"]).to(dev)
+        per_copy = L0.numel() * 4
+        ncopy = max(1, math.ceil(ROTATE_BYTES / per_copy))
+        srcs = [L0] + [L0.clone() for _ in range(ncopy - 1)]
+    out = lbs.alloc_outputs(p, device=dev)
+    ws = lbs.alloc_workspace(p, device=dev)
+    dlogits = torch.empty((w.T, w.E), dtype=torch.float32, device=dev) if w.backward else None
+
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    hev = HipEvents()
+    K = args.steps
+    ev_rows = [(hev.create(), hev.create()) for _ in range(K)]
+    ev_bwd = [(hev.create(), hev.create()) for _ in range(K)] if w.backward else None
+
+    def step(i, timed):
+        src = srcs[i % ncopy]
+        kw = dict(X=src, Wg=Wg) if w.d > 0 else dict(logits=src)
+        lbs.moe_route(p, out, ws, stream=stream, row_pass_events=ev_rows[i] if timed else None, **kw)
+        if w.backward:
+            L = out["logits"] if w.d > 0 else src
+            if timed:
+                hev.record(ev_bwd[i][0], sh)
+            lbs.moe_route_backward(p, L, out["counts"], dlogits, row_stats=out["row_stats"],
+                                   stream=stream)
+            if timed:
+                hev.record(ev_bwd[i][1], sh)
+
+    for i in range(args.warmup):
+        step(i, False)
+    torch.cuda.synchronize()
+
+    # Let the host enqueue every timed step while the GPU is still busy, so
+    # that the timed region measures the GPU and not the Python launch rate.
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(int(2e8))
+    t_start.record(stream)
+    h0 = time.perf_counter()
+    for i in range(K):
+        step(i, True)
+    host_s = time.perf_counter() - h0
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / K
+    rows_ms = sum(hev.elapsed_ms(a, b) for a, b in ev_rows) / K
+    bwd_ms = sum(hev.elapsed_ms(a, b) for a, b in ev_bwd) / K if w.backward else None
+    status = int(out["status"].item())
+
+    # device-to-device copy ceiling (same rotation logic: 1 GiB buffers)
+    cbuf = torch.empty(256 * 1024 * 1024, dtype=torch.float32, device=dev)
+    cdst = torch.empty_like(cbuf)
+    for _ in range(3):
+        cdst.copy_(cbuf)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(10):
+        cdst.copy_(cbuf)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * cbuf.numel() * 4 * 10 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del cbuf, cdst
+
+    ab = alg_bytes(w, w.T)
+    if w.d > 0:
+        dom_name, dom_bytes, dom_ms = "gate+route forward (no per-kernel split)", ab["forward"], ms_step
+    elif w.backward and bwd_ms > rows_ms:
+        dom_name, dom_bytes, dom_ms = "route_backward_kernel", ab["backward"], bwd_ms
+    else:
+        dom_name, dom_bytes, dom_ms = "route_rows_kernel", ab["rows"], rows_ms
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    step_bytes = ab["forward"] + ab["backward"]
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(w, inp, args.cpu_seconds)
+
+    res = {
+        "metric": METRIC,
+        "value": w.T / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w.d == 0 else "bf16-in/f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "T": w.T, "E": w.E, "k": w.k, "n_micro": w.n_micro,
+                   "d": w.d, "capacity_factor": w.capacity_factor, "alpha": w.alpha,
+                   "renorm": w.renorm, "backward": w.backward},
+        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": None, "alg_bytes_per_launch": dom_bytes,
+                     "launch_ms": round(dom_ms, 5)},
+        "cpu_baseline": cpu,
+        "detail": {"step_alg_bytes": step_bytes,
+                   "step_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+                   "row_pass_ms": round(rows_ms, 5),
+                   "backward_ms": None if bwd_ms is None else round(bwd_ms, 5),
+                   "copy_ceiling_GBps": round(copy_gbps, 1),
+                   "assignments_per_s": w.T * w.k / (ms_step * 1e-3),
+                   "input_copies": ncopy, "host_enqueue_s": round(host_s, 4),
+                   "status": status},
+    }
+    print(json.dumps(res), flush=True)
+    for a, b in ev_rows:
+        hev.destroy(a); hev.destroy(b)
+    if ev_bwd:
+        for a, b in ev_bwd:
+            hev.destroy(a); hev.destroy(b)
+
+
+if __name__ == "__main__":
+    main()

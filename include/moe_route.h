@@ -1,0 +1,176 @@
+/*
+ * moe_route.h -- C ABI of the MI355X (gfx950) MoE routing library:
+ * token-to-expert routing with equal-cost load-balancing statistics.
+ *
+ * Pages cited (address, subject, section):
+ *   [p1] mhpq.cn/news/998159 -- three layers of HPC load balancing; MoE
+ *        part 4.2 (softmax router, argmax/top-k, f_i, P_i, aux loss), 4.4
+ *        (top-k version: f_i over T*k assignments, histogram), 4.5 (capacity
+ *        and token drop), 5.3/5.4 (f and P sum to one; max/mean load).
+ *   [p2] codechina.net article 413310 -- equal-cost balancing in MoE
+ *        training: 2.2 (L_aux = alpha*N*sum_i f_i*P_i; gradient only
+ *        through P), 3.1 (histogram keeps zero-count experts), 3.2 (aux loss
+ *        only in training), 4.2 (distribution ratio, entropy of the load).
+ *   [p3] cnvsn.com/news/335486 -- load-balancing survey: 3.1 and 5.1
+ *        (coefficient of variation, load-balance degree).
+ *
+ * Conventions shared by every entry point:
+ *   - Every array pointer is a DEVICE pointer to memory that the caller
+ *     allocated and owns; the library never allocates, frees or keeps a
+ *     pointer past the call.  Arrays are dense and row-major.
+ *   - "stream" is a hipStream_t passed as an opaque pointer (NULL = the
+ *     default stream).  All device work is enqueued asynchronously on it;
+ *     no call synchronises the device.
+ *   - Arguments are validated on the host before anything is enqueued; on
+ *     an error code nothing is launched and no output is touched.
+ *   - T = tokens, E = experts, k = experts per token, m = n_micro
+ *     microbatches of Tm = T/m tokens; each microbatch is routed on its own.
+ *   - Ties between equal logits go to the lower expert index; -0.0 and +0.0
+ *     are equal.  Results are deterministic: no floating-point atomics.
+ */
+#ifndef MOE_ROUTE_H
+#define MOE_ROUTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ROUTE_MAX_E 1024
+#define MOE_ROUTE_MAX_K 32
+
+/* Return codes. */
+#define MOE_OK               0
+#define MOE_ERR_INVALID_ARG (-1) /* NULL required pointer, bad shape or value */
+#define MOE_ERR_UNSUPPORTED (-2) /* E, k or gate shape beyond the limits      */
+#define MOE_ERR_WORKSPACE   (-3) /* workspace NULL or smaller than required   */
+#define MOE_ERR_HIP         (-4) /* a HIP launch or runtime call failed       */
+
+/* moe_route_params.flags */
+#define MOE_RENORM_TOPK    1u /* rescale the k gate weights to sum to 1     */
+#define MOE_SAVE_ROW_STATS 2u /* write per-token softmax (max, sum)         */
+#define MOE_WRITE_INV_PERM 4u /* write inv_perm                             */
+
+/* Bits of the optional status word (set for the whole call). */
+#define MOE_STATUS_NONFINITE 1 /* a row had a NaN/+inf logit, or only -inf;
+                                  outputs for such rows are unspecified     */
+#define MOE_STATUS_INTERNAL  2 /* an internal bound check tripped          */
+
+typedef struct {
+    int32_t  T, E, k, n_micro; /* 1 <= k <= E <= MOE_ROUTE_MAX_E, k <= MOE_ROUTE_MAX_K,
+                                  T % n_micro == 0, T*k < 2^31 */
+    int32_t  d;                /* 0: logits are given; > 0: gate path, logits = X[T,d].Wg[d,E] */
+    float    capacity_factor;  /* used when capacity < 0; <= 0 means no limit */
+    int32_t  capacity;         /* >= 0: per-microbatch capacity C; -1: from capacity_factor */
+    float    alpha;            /* aux-loss weight; 0 is legal (aux = 0, gradient = 0) */
+    uint32_t flags;            /* MOE_* flags above */
+} moe_route_params;
+
+/*
+ * Outputs of moe_route.  Arrays not marked "nullable" are required.
+ *   topk_idx [T,k] int32   experts of token t, best first ([p1] 4.2, 4.4)
+ *   topk_w   [T,k] fp32    gate weights: softmax probability of the pick,
+ *                          or that divided by the sum over the k picks
+ *                          (MOE_RENORM_TOPK)
+ *   logits   [T,E] fp32    gate path only: the X.Wg logits are written here
+ *                          (required when d > 0, ignored otherwise)
+ *   row_stats[T,2] fp32    nullable; (max, sum of exp(l - max)) per token,
+ *                          written when MOE_SAVE_ROW_STATS is set
+ *   counts   [m,E] int32   assignments per expert before capacity
+ *                          ([p1] 4.4, [p2] 3.1 -- zero-count experts kept)
+ *   offsets  [m,E+1] int32 exclusive prefix sum of counts (segment-local)
+ *   perm     [T*k] int32   expert-sorted dispatch order: the segment
+ *                          [mb*Tm*k, (mb+1)*Tm*k) lists the flat indices
+ *                          t*k+j of microbatch mb grouped by expert, experts
+ *                          ascending, (t, j) ascending inside an expert
+ *   inv_perm [T*k] int32   nullable; position in perm of assignment t*k+j,
+ *                          written when MOE_WRITE_INV_PERM is set
+ *   dropped  [T*k] uint8   1 when the assignment is the (C+1)-th or later of
+ *                          its expert in its microbatch ([p1] 4.5)
+ *   f, P     [m,E] fp32    nullable; f_e = counts/(Tm*k); P_e = mean over
+ *                          the microbatch's tokens of softmax_e ([p1] 4.2)
+ *   aux_loss [m] fp32      alpha * E * sum_e f_e * P_e ([p2] 2.2)
+ *   cv       [m] fp32      population std / mean of counts ([p3] 3.1)
+ *   max_over_mean [m] fp32 max(counts) / mean ([p1] 5.4)
+ *   extra_stats [m,8] fp32 nullable; min/mean, balance degree
+ *                          1-(max-mean)/mean ([p3] 5.1), entropy of f (nats,
+ *                          [p2] 4.2), kept, dropped, C (-1 = unlimited),
+ *                          max f, min f ([p2] 4.2)
+ *   status   [1] int32     nullable; MOE_STATUS_* bits of this call
+ *   row_pass_events        nullable pair of hipEvent_t handles created by the
+ *                          caller; when both are set the library records
+ *                          them on the stream right before and right after
+ *                          the row-pass kernel (per-kernel timing)
+ */
+typedef struct {
+    int32_t *topk_idx;
+    float   *topk_w;
+    float   *logits;
+    float   *row_stats;
+    int32_t *counts;
+    int32_t *offsets;
+    int32_t *perm;
+    int32_t *inv_perm;
+    uint8_t *dropped;
+    float   *f;
+    float   *P;
+    float   *aux_loss;
+    float   *cv;
+    float   *max_over_mean;
+    float   *extra_stats;
+    int32_t *status;
+    void    *row_pass_events[2];
+} moe_route_out;
+
+/*
+ * Bytes of device workspace moe_route needs for these parameters (written to
+ * *bytes).  The workspace holds per-block partial histograms and probability
+ * sums; it needs no initialisation and its contents are scratch.
+ */
+int moe_route_workspace_size(const moe_route_params *p, size_t *bytes);
+
+/*
+ * Per-microbatch capacity C for these parameters (host only, no device
+ * work): C = ceil(cf * ceil(Tm*k/E)) from [p1] 4.5 with the k picks of a
+ * token counted as k assignments; -1 when unlimited; the explicit capacity
+ * field wins when >= 0.
+ */
+int moe_route_capacity(const moe_route_params *p, int32_t *capacity);
+
+/*
+ * Forward routing ([p1] 4.2-4.5, [p2] 2.2, [p3] 3.1/5.1).
+ * logits [T,E] fp32 when p->d == 0 (X, Wg ignored); when p->d > 0, X [T,d]
+ * and Wg [d,E] are bf16 bit patterns (uint16) and out->logits receives
+ * X.Wg accumulated in fp32 (logits ignored).  Enqueues the whole forward on
+ * stream.  workspace: device buffer of at least moe_route_workspace_size()
+ * bytes, used only during the call's kernels (calls sharing one workspace
+ * must be ordered on one stream).
+ */
+int moe_route(const moe_route_params *p, const float *logits, const uint16_t *X,
+              const uint16_t *Wg, const moe_route_out *out, void *workspace,
+              size_t workspace_bytes, void *stream);
+
+/*
+ * Gradient of the aux loss with respect to the logits ([p1] 4.2: f carries
+ * no gradient, P does; [p2] 2.2):
+ *   dlogits[t,j] = g_mb * alpha * E / Tm * p[t,j] * (f_j - sum_i f_i p[t,i])
+ * logits [T,E] fp32 (for the gate path: the logits moe_route wrote);
+ * row_stats [T,2] nullable (the forward's MOE_SAVE_ROW_STATS output; NULL
+ * recomputes them); counts [m,E] the forward's counts; d_aux [m] nullable
+ * upstream gradient of each microbatch's aux loss (NULL = 1); dlogits
+ * [T,E] fp32 output.  p->capacity_factor, capacity and flags are ignored.
+ */
+int moe_route_backward(const moe_route_params *p, const float *logits,
+                       const float *row_stats, const int32_t *counts,
+                       const float *d_aux, float *dlogits, void *stream);
+
+/* Static message for a return code. */
+const char *moe_route_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ROUTE_H */

@@ -1,0 +1,185 @@
+"""ctypes binding of the C ABI in ``include/moe_route.h`` (same names).
+
+Argument marshalling only: every step of routing runs in the HIP library
+``_lib/libmoe_route.so``.  PyTorch supplies device memory and the stream.
+There is no fallback: if the library is missing or a call fails, an exception
+is raised.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libmoe_route.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = -1
+MOE_ERR_UNSUPPORTED = -2
+MOE_ERR_WORKSPACE = -3
+MOE_ERR_HIP = -4
+
+MOE_RENORM_TOPK = 1
+MOE_SAVE_ROW_STATS = 2
+MOE_WRITE_INV_PERM = 4
+
+MOE_STATUS_NONFINITE = 1
+MOE_STATUS_INTERNAL = 2
+
+MOE_ROUTE_MAX_E = 1024
+MOE_ROUTE_MAX_K = 32
+
+EXPORTED = ("moe_route_workspace_size", "moe_route_capacity", "moe_route",
+            "moe_route_backward", "moe_route_strerror")
+
+
+class MoeRouteError(RuntimeError):
+    def __init__(self, code, func):
+        self.code = code
+        super().__init__(f"{func} failed ({code}): {moe_route_strerror(code)}")
+
+
+class moe_route_params(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("n_micro", ctypes.c_int32), ("d", ctypes.c_int32),
+                ("capacity_factor", ctypes.c_float), ("capacity", ctypes.c_int32),
+                ("alpha", ctypes.c_float), ("flags", ctypes.c_uint32)]
+
+
+_OUT_FIELDS = ("topk_idx", "topk_w", "logits", "row_stats", "counts", "offsets", "perm",
+               "inv_perm", "dropped", "f", "P", "aux_loss", "cv", "max_over_mean",
+               "extra_stats", "status")
+
+
+class moe_route_out(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in _OUT_FIELDS] + [
+        ("row_pass_events", ctypes.c_void_p * 2)]
+
+
+_lib = None
+
+
+def load(path=None):
+    """Load the HIP routing library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    # PyTorch first: its HIP runtime (same soname) then serves this library
+    # too, so device pointers and streams are shared by one runtime.
+    import torch  # noqa: F401
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"HIP routing library not built: {p} is missing "
+                           "(run load_balancing_statistics_amd.build.build())")
+    lib = ctypes.CDLL(p)
+    P = ctypes.POINTER(moe_route_params)
+    vp = ctypes.c_void_p
+    lib.moe_route_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.moe_route_workspace_size.restype = ctypes.c_int
+    lib.moe_route_capacity.argtypes = [P, ctypes.POINTER(ctypes.c_int32)]
+    lib.moe_route_capacity.restype = ctypes.c_int
+    lib.moe_route.argtypes = [P, vp, vp, vp, ctypes.POINTER(moe_route_out), vp, ctypes.c_size_t, vp]
+    lib.moe_route.restype = ctypes.c_int
+    lib.moe_route_backward.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    lib.moe_route_backward.restype = ctypes.c_int
+    lib.moe_route_strerror.argtypes = [ctypes.c_int]
+    lib.moe_route_strerror.restype = ctypes.c_char_p
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def make_params(T, E, k, n_micro=1, d=0, capacity_factor=1.0, capacity=-1, alpha=0.01,
+                renorm=False, save_row_stats=False, inv_perm=False):
+    flags = ((MOE_RENORM_TOPK if renorm else 0) | (MOE_SAVE_ROW_STATS if save_row_stats else 0)
+             | (MOE_WRITE_INV_PERM if inv_perm else 0))
+    return moe_route_params(int(T), int(E), int(k), int(n_micro), int(d), float(capacity_factor),
+                            int(capacity), float(alpha), flags)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(getattr(stream, "cuda_stream", stream))
+
+
+def moe_route_strerror(code):
+    return load().moe_route_strerror(int(code)).decode()
+
+
+def moe_route_workspace_size(params):
+    n = ctypes.c_size_t(0)
+    rc = load().moe_route_workspace_size(ctypes.byref(params), ctypes.byref(n))
+    if rc != MOE_OK:
+        raise MoeRouteError(rc, "moe_route_workspace_size")
+    return n.value
+
+
+def moe_route_capacity(params):
+    c = ctypes.c_int32(0)
+    rc = load().moe_route_capacity(ctypes.byref(params), ctypes.byref(c))
+    if rc != MOE_OK:
+        raise MoeRouteError(rc, "moe_route_capacity")
+    return c.value
+
+
+def moe_route(params, out, workspace, logits=None, X=None, Wg=None, stream=None,
+              row_pass_events=None):
+    """Forward routing; ``out`` maps output names to device tensors (or None).
+
+    ``row_pass_events``: optional pair of raw hipEvent_t handles (ints) that the
+    library records around the row-pass kernel."""
+    o = moe_route_out(*[None if out.get(n) is None else out[n].data_ptr() for n in _OUT_FIELDS])
+    if row_pass_events is not None:
+        o.row_pass_events[0] = row_pass_events[0]
+        o.row_pass_events[1] = row_pass_events[1]
+    rc = load().moe_route(ctypes.byref(params), _ptr(logits), _ptr(X), _ptr(Wg), ctypes.byref(o),
+                          _ptr(workspace), workspace.numel() * workspace.element_size()
+                          if workspace is not None else 0, _stream(stream))
+    if rc != MOE_OK:
+        raise MoeRouteError(rc, "moe_route")
+
+
+def moe_route_backward(params, logits, counts, dlogits, row_stats=None, d_aux=None, stream=None):
+    """Aux-loss gradient with respect to the logits, written into ``dlogits``."""
+    rc = load().moe_route_backward(ctypes.byref(params), _ptr(logits), _ptr(row_stats),
+                                   _ptr(counts), _ptr(d_aux), _ptr(dlogits), _stream(stream))
+    if rc != MOE_OK:
+        raise MoeRouteError(rc, "moe_route_backward")
+
+
+def alloc_outputs(params, device="cuda"):
+    """Device tensors for every output of ``moe_route`` (plumbing only)."""
+    import torch
+    T, E, k, m = params.T, params.E, params.k, params.n_micro
+    i32, f32 = torch.int32, torch.float32
+    out = dict(
+        topk_idx=torch.empty((T, k), dtype=i32, device=device),
+        topk_w=torch.empty((T, k), dtype=f32, device=device),
+        logits=torch.empty((T, E), dtype=f32, device=device) if params.d > 0 else None,
+        row_stats=torch.empty((T, 2), dtype=f32, device=device)
+        if params.flags & MOE_SAVE_ROW_STATS else None,
+        counts=torch.empty((m, E), dtype=i32, device=device),
+        offsets=torch.empty((m, E + 1), dtype=i32, device=device),
+        perm=torch.empty(T * k, dtype=i32, device=device),
+        inv_perm=torch.empty(T * k, dtype=i32, device=device)
+        if params.flags & MOE_WRITE_INV_PERM else None,
+        dropped=torch.empty(T * k, dtype=torch.uint8, device=device),
+        f=torch.empty((m, E), dtype=f32, device=device),
+        P=torch.empty((m, E), dtype=f32, device=device),
+        aux_loss=torch.empty(m, dtype=f32, device=device),
+        cv=torch.empty(m, dtype=f32, device=device),
+        max_over_mean=torch.empty(m, dtype=f32, device=device),
+        extra_stats=torch.empty((m, 8), dtype=f32, device=device),
+        status=torch.empty(1, dtype=i32, device=device),
+    )
+    return out
+
+
+def alloc_workspace(params, device="cuda"):
+    import torch
+    n = moe_route_workspace_size(params)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)

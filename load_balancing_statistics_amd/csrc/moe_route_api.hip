@@ -1,0 +1,170 @@
+// moe_route_api.hip -- the C ABI declared in include/moe_route.h: argument
+// validation on the host, workspace sizing, and the launch sequence
+//   [gate transpose + gate GEMM] -> row pass -> block scan -> scatter/stats
+// for the forward, and the single streaming pass of the backward.
+#include <climits>
+#include <cmath>
+
+#include "route_common.hpp"
+
+namespace {
+
+using moe::RowCfg;
+
+constexpr uint32_t kKnownFlags = MOE_RENORM_TOPK | MOE_SAVE_ROW_STATS | MOE_WRITE_INV_PERM;
+constexpr size_t kMaxLds = 160 * 1024;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_shape(const moe_route_params* p) {
+    if (!p) return MOE_ERR_INVALID_ARG;
+    if (p->T < 1 || p->E < 1 || p->k < 1 || p->n_micro < 1 || p->d < 0) return MOE_ERR_INVALID_ARG;
+    if (p->k > p->E || p->T % p->n_micro != 0) return MOE_ERR_INVALID_ARG;
+    if (p->E > MOE_ROUTE_MAX_E || p->k > MOE_ROUTE_MAX_K) return MOE_ERR_UNSUPPORTED;
+    if (int64_t(p->T) * p->k > INT_MAX) return MOE_ERR_UNSUPPORTED;
+    if (!std::isfinite(p->alpha) || !std::isfinite(p->capacity_factor)) return MOE_ERR_INVALID_ARG;
+    if (p->capacity < -1) return MOE_ERR_INVALID_ARG;
+    if (p->flags & ~kKnownFlags) return MOE_ERR_INVALID_ARG;
+    if (p->d > 0 && !moe::gate_supported(p->T, p->d, p->E)) return MOE_ERR_UNSUPPORTED;
+    const RowCfg c = moe::choose_rows(p->T, p->E, p->k, p->n_micro);
+    if (c.G < 0 || moe::rows_lds_bytes(c, p->E, p->k) > kMaxLds) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int64_t capacity_of(const moe_route_params* p) {
+    if (p->capacity >= 0) return p->capacity;
+    if (!(p->capacity_factor > 0.f)) return -1;
+    const int64_t Tm = p->T / p->n_micro;
+    const int64_t per_expert = (Tm * p->k + p->E - 1) / p->E;
+    const double c = std::ceil(double(p->capacity_factor) * double(per_expert));
+    return c > double(INT_MAX) ? INT_MAX : int64_t(c);
+}
+
+size_t workspace_bytes(const moe_route_params* p, const RowCfg& c) {
+    const size_t gate = p->d > 0 ? moe::gate_workspace_bytes(p->d, p->E) : 0;
+    return moe::carve_workspace(nullptr, c.B, p->E, p->n_micro, gate).bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_route_workspace_size(const moe_route_params* p, size_t* bytes) {
+    const int rc = check_shape(p);
+    if (rc != MOE_OK) return rc;
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    *bytes = workspace_bytes(p, moe::choose_rows(p->T, p->E, p->k, p->n_micro));
+    return MOE_OK;
+}
+
+int moe_route_capacity(const moe_route_params* p, int32_t* capacity) {
+    const int rc = check_shape(p);
+    if (rc != MOE_OK) return rc;
+    if (!capacity) return MOE_ERR_INVALID_ARG;
+    *capacity = int32_t(capacity_of(p));
+    return MOE_OK;
+}
+
+int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
+              const uint16_t* Wg, const moe_route_out* out, void* workspace,
+              size_t workspace_bytes_given, void* stream) {
+    int rc = check_shape(p);
+    if (rc != MOE_OK) return rc;
+    if (!out) return MOE_ERR_INVALID_ARG;
+    const bool gate = p->d > 0;
+    if (gate) {
+        if (!X || !Wg || !out->logits) return MOE_ERR_INVALID_ARG;
+        if (!aligned(X, 16) || !aligned(Wg, 2) || !aligned(out->logits, 4)) return MOE_ERR_INVALID_ARG;
+    } else {
+        if (!logits || !aligned(logits, 4)) return MOE_ERR_INVALID_ARG;
+    }
+    if (!out->topk_idx || !out->topk_w || !out->counts || !out->offsets || !out->perm ||
+        !out->dropped || !out->aux_loss || !out->cv || !out->max_over_mean)
+        return MOE_ERR_INVALID_ARG;
+    if ((p->flags & MOE_SAVE_ROW_STATS) && !out->row_stats) return MOE_ERR_INVALID_ARG;
+    if ((p->flags & MOE_WRITE_INV_PERM) && !out->inv_perm) return MOE_ERR_INVALID_ARG;
+    const void* fptrs[] = {out->topk_idx, out->topk_w, out->row_stats, out->counts, out->offsets,
+                           out->perm, out->inv_perm, out->f, out->P, out->aux_loss, out->cv,
+                           out->max_over_mean, out->extra_stats, out->status};
+    for (const void* q : fptrs)
+        if (q && !aligned(q, 4)) return MOE_ERR_INVALID_ARG;
+
+    const RowCfg c = moe::choose_rows(p->T, p->E, p->k, p->n_micro);
+    const size_t need = workspace_bytes(p, c);
+    if (!workspace || workspace_bytes_given < need || !aligned(workspace, 256)) return MOE_ERR_WORKSPACE;
+    const moe::Workspace ws = moe::carve_workspace(
+        workspace, c.B, p->E, p->n_micro, gate ? moe::gate_workspace_bytes(p->d, p->E) : 0);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int Tm = p->T / p->n_micro;
+
+    const float* L = logits;
+    if (gate) {
+        moe::GateArgs g{X, Wg, out->logits, p->T, p->d, p->E};
+        if (moe::launch_gate_gemm(g, ws.Wt, st) != hipSuccess) return MOE_ERR_HIP;
+        L = out->logits;
+    }
+
+    moe::RowsArgs ra{};
+    ra.logits = L;
+    ra.T = p->T; ra.E = p->E; ra.k = p->k; ra.Tm = Tm; ra.R = c.R; ra.bpm = c.bpm;
+    ra.renorm = (p->flags & MOE_RENORM_TOPK) ? 1 : 0;
+    ra.save_stats = (p->flags & MOE_SAVE_ROW_STATS) ? 1 : 0;
+    ra.topk_idx = out->topk_idx; ra.topk_w = out->topk_w; ra.row_stats = out->row_stats;
+    ra.cnt_part = ws.cnt_part; ra.P_part = ws.P_part; ra.flag_part = ws.flag_part;
+    const bool timed = out->row_pass_events[0] && out->row_pass_events[1];
+    if (timed && hipEventRecord(static_cast<hipEvent_t>(out->row_pass_events[0]), st) != hipSuccess)
+        return MOE_ERR_HIP;
+    if (moe::launch_route_rows(c, ra, st) != hipSuccess) return MOE_ERR_HIP;
+    if (timed && hipEventRecord(static_cast<hipEvent_t>(out->row_pass_events[1]), st) != hipSuccess)
+        return MOE_ERR_HIP;
+
+    moe::ScanArgs sa{};
+    sa.cnt_part = ws.cnt_part; sa.P_part = ws.P_part; sa.flag_part = ws.flag_part;
+    sa.E = p->E; sa.bpm = c.bpm; sa.n_micro = p->n_micro; sa.B = c.B;
+    sa.colprefix = ws.colprefix; sa.totals = ws.totals; sa.Psum = ws.Psum; sa.status = out->status;
+    if (moe::launch_route_scan(c, sa, st) != hipSuccess) return MOE_ERR_HIP;
+
+    moe::ScatterArgs ca{};
+    ca.topk_idx = out->topk_idx; ca.colprefix = ws.colprefix; ca.totals = ws.totals; ca.Psum = ws.Psum;
+    ca.T = p->T; ca.E = p->E; ca.k = p->k; ca.Tm = Tm; ca.R = c.R; ca.bpm = c.bpm;
+    ca.capacity = int(capacity_of(p)); ca.alpha = p->alpha;
+    ca.counts = out->counts; ca.offsets = out->offsets; ca.perm = out->perm;
+    ca.inv_perm = (p->flags & MOE_WRITE_INV_PERM) ? out->inv_perm : nullptr;
+    ca.dropped = out->dropped; ca.f = out->f; ca.P = out->P; ca.aux = out->aux_loss; ca.cv = out->cv;
+    ca.max_over_mean = out->max_over_mean; ca.extra = out->extra_stats; ca.status = out->status;
+    if (moe::launch_route_scatter(c, ca, st) != hipSuccess) return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+int moe_route_backward(const moe_route_params* p, const float* logits, const float* row_stats,
+                       const int32_t* counts, const float* d_aux, float* dlogits, void* stream) {
+    if (!p) return MOE_ERR_INVALID_ARG;
+    moe_route_params q = *p;
+    q.d = 0;  // the backward reads logits whatever produced them
+    const int rc = check_shape(&q);
+    if (rc != MOE_OK) return rc;
+    if (!logits || !counts || !dlogits) return MOE_ERR_INVALID_ARG;
+    const void* ptrs[] = {logits, row_stats, counts, d_aux, dlogits};
+    for (const void* x : ptrs)
+        if (x && !aligned(x, 4)) return MOE_ERR_INVALID_ARG;
+    const RowCfg c = moe::choose_rows(q.T, q.E, q.k, q.n_micro);
+    moe::BackArgs b{};
+    b.logits = logits; b.row_stats = row_stats; b.counts = counts; b.d_aux = d_aux; b.dlogits = dlogits;
+    b.T = q.T; b.E = q.E; b.k = q.k; b.Tm = q.T / q.n_micro; b.R = c.R; b.bpm = c.bpm;
+    b.alpha = q.alpha;
+    if (moe::launch_route_backward(c, b, static_cast<hipStream_t>(stream)) != hipSuccess) return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+const char* moe_route_strerror(int code) {
+    switch (code) {
+        case MOE_OK: return "success";
+        case MOE_ERR_INVALID_ARG: return "invalid argument (NULL pointer, misaligned pointer, bad shape or value)";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape (E, k, T*k or gate dimensions beyond the limits)";
+        case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than moe_route_workspace_size()";
+        case MOE_ERR_HIP: return "a HIP kernel launch failed";
+        default: return "unknown moe_route error code";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,378 @@
+// route_common.hpp -- launch configuration, kernel argument blocks and
+// wavefront helpers shared by the gfx950 routing kernels.
+//
+// Data layout: logits [T,E] fp32 row-major.  A row is handled by a
+// "segment" of S lanes of a 64-lane wavefront; lane s of the segment owns the
+// G columns c = g*S + s (g < G), so each load instruction of a segment reads
+// S consecutive floats of one row and a wave reads 64/S rows at once.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_route.h"
+
+namespace moe {
+
+// ----------------------------------------------------------------- config
+struct RowCfg {
+    int S;      // lanes per row (power of two, >= k)
+    int G;      // columns per lane
+    int NW;     // waves per block
+    int R;      // rows per block
+    int bpm;    // blocks per microbatch
+    int B;      // blocks in total (= n_micro * bpm)
+};
+
+// Column counts per lane that have kernel instantiations.
+constexpr int kGTable[] = {1, 2, 4, 8, 12, 16, 24};
+constexpr int kGMax = 24;
+
+inline int next_pow2(int v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+inline int round_g(int g) {
+    for (int t : kGTable)
+        if (g <= t) return t;
+    return -1;
+}
+
+// Pick the lane mapping: the narrowest segment (S >= k, power of two) whose
+// per-lane column count fits the table; then rows per block so that large
+// workloads launch on the order of a thousand blocks.
+inline RowCfg choose_rows(int T, int E, int k, int n_micro) {
+    RowCfg c{};
+    int S = next_pow2(k < 1 ? 1 : k);
+    while (S < 64 && (E + S - 1) / S > kGMax) S <<= 1;
+    c.S = S;
+    c.G = round_g((E + S - 1) / S);
+    c.NW = 8;
+    const int W = 64 / S;
+    const int per_iter = c.NW * W;
+    const long Tm = T / n_micro;
+    long iters = (long(T) + per_iter * 1024L - 1) / (per_iter * 1024L);
+    if (iters < 1) iters = 1;
+    if (iters > 16) iters = 16;
+    long R = per_iter * iters;
+    if (R > Tm) R = ((Tm + per_iter - 1) / per_iter) * per_iter;
+    c.R = int(R);
+    c.bpm = int((Tm + R - 1) / R);
+    c.B = c.bpm * n_micro;
+    return c;
+}
+
+// Candidate-list capacity per row for the threshold top-k (see route_rows).
+__host__ __device__ constexpr int cand_cap(int S, int G) {
+    return (S * G < (2 * S > 32 ? 2 * S : 32)) ? S * G : (2 * S > 32 ? 2 * S : 32);
+}
+
+// LDS row stride (floats) of the row copy: S times an odd number >= G, so
+// the segments of a wave start on distinct banks.
+__host__ __device__ constexpr int row_stride(int S, int G) { return S * (G | 1); }
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline size_t rows_lds_bytes(const RowCfg& c, int E, int k) {
+    const int W = 64 / c.S;
+    size_t hist = align_up(size_t(E) * 4, 16);
+    size_t rowbuf = size_t(c.NW) * W * row_stride(c.S, c.G) * 4;
+    size_t cand = size_t(c.NW) * W * (cand_cap(c.S, c.G) + 1) * 8;
+    size_t sel = size_t(c.NW) * W * k * 8;
+    return hist + align_up(rowbuf, 16) + cand + sel;
+}
+
+// Workspace carve-up (each piece 256-byte aligned).
+struct Workspace {
+    int32_t* cnt_part;    // [B,E]   per-block histograms
+    float*   P_part;      // [B,E]   per-block probability sums
+    int32_t* flag_part;   // [B]     per-block status bits
+    int32_t* colprefix;   // [B,E]   exclusive prefix over blocks of the microbatch
+    int32_t* totals;      // [m,E]   counts per microbatch
+    double*  Psum;        // [m,E]   probability sums per microbatch
+    uint16_t* Wt;         // [E,d]   transposed gate weights (gate path only)
+    size_t   bytes;
+};
+
+inline Workspace carve_workspace(void* base, int B, int E, int m, size_t gate_bytes) {
+    Workspace w{};
+    size_t off = 0;
+    auto take = [&](size_t n) {
+        size_t o = off;
+        off = align_up(off + n, 256);
+        return o;
+    };
+    size_t o_cnt = take(size_t(B) * E * 4);
+    size_t o_P = take(size_t(B) * E * 4);
+    size_t o_flag = take(size_t(B) * 4);
+    size_t o_pre = take(size_t(B) * E * 4);
+    size_t o_tot = take(size_t(m) * E * 4);
+    size_t o_ps = take(size_t(m) * E * 8);
+    size_t o_wt = take(gate_bytes);
+    w.bytes = off;
+    char* b = static_cast<char*>(base);
+    if (b) {
+        w.cnt_part = reinterpret_cast<int32_t*>(b + o_cnt);
+        w.P_part = reinterpret_cast<float*>(b + o_P);
+        w.flag_part = reinterpret_cast<int32_t*>(b + o_flag);
+        w.colprefix = reinterpret_cast<int32_t*>(b + o_pre);
+        w.totals = reinterpret_cast<int32_t*>(b + o_tot);
+        w.Psum = reinterpret_cast<double*>(b + o_ps);
+        w.Wt = gate_bytes ? reinterpret_cast<uint16_t*>(b + o_wt) : nullptr;
+    }
+    return w;
+}
+
+// ------------------------------------------------------- kernel arguments
+struct RowsArgs {
+    const float* logits;
+    int T, E, k, Tm, R, bpm;
+    int renorm, save_stats;
+    int32_t* topk_idx;
+    float* topk_w;
+    float* row_stats;
+    int32_t* cnt_part;
+    float* P_part;
+    int32_t* flag_part;
+};
+
+struct ScanArgs {
+    const int32_t* cnt_part;
+    const float* P_part;
+    const int32_t* flag_part;
+    int E, bpm, n_micro, B;
+    int32_t* colprefix;
+    int32_t* totals;
+    double* Psum;
+    int32_t* status;
+};
+
+struct ScatterArgs {
+    const int32_t* topk_idx;
+    const int32_t* colprefix;
+    const int32_t* totals;
+    const double* Psum;
+    int T, E, k, Tm, R, bpm;
+    int capacity;  // < 0: unlimited
+    float alpha;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* perm;
+    int32_t* inv_perm;
+    uint8_t* dropped;
+    float* f;
+    float* P;
+    float* aux;
+    float* cv;
+    float* max_over_mean;
+    float* extra;
+    int32_t* status;
+};
+
+struct BackArgs {
+    const float* logits;
+    const float* row_stats;
+    const int32_t* counts;
+    const float* d_aux;
+    float* dlogits;
+    int T, E, k, Tm, R, bpm;
+    float alpha;
+};
+
+struct GateArgs {
+    const uint16_t* X;
+    const uint16_t* Wg;
+    float* logits;
+    int T, d, E;
+};
+
+// Launchers (each defined next to its kernel).  Return a hipError_t.
+hipError_t launch_route_rows(const RowCfg& c, const RowsArgs& a, hipStream_t st);
+hipError_t launch_route_scan(const RowCfg& c, const ScanArgs& a, hipStream_t st);
+hipError_t launch_route_scatter(const RowCfg& c, const ScatterArgs& a, hipStream_t st);
+hipError_t launch_route_backward(const RowCfg& c, const BackArgs& a, hipStream_t st);
+hipError_t launch_gate_gemm(const GateArgs& a, uint16_t* wt, hipStream_t st);
+bool gate_supported(int T, int d, int E);
+size_t gate_workspace_bytes(int d, int E);
+
+}  // namespace moe
+
+// ------------------------------------------------------- device helpers
+#ifdef __HIP_DEVICE_COMPILE__
+#define MOE_DEV __device__ __forceinline__
+#else
+#define MOE_DEV __device__ inline
+#endif
+
+namespace moe {
+namespace dev {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// DPP move with a compile-time control word (row/bank masks full).
+template <int CTRL>
+MOE_DEV float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+MOE_DEV int dppi(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+// Partner value for a butterfly step of distance D inside aligned groups of
+// 2D lanes.  D = 1, 2 use quad permutes; D = 4, 8 use the half-row / row
+// mirrors (partner in the other half of the 8- or 16-lane group, which is
+// all an all-reduce needs); D = 16 a swizzle; D = 32 a bpermute.
+template <int D>
+MOE_DEV float xstep(float v) {
+    if constexpr (D == 1) return dpp<0xB1>(v);        // quad_perm [1,0,3,2]
+    else if constexpr (D == 2) return dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    else if constexpr (D == 4) return dpp<0x141>(v);  // row_half_mirror
+    else if constexpr (D == 8) return dpp<0x140>(v);  // row_mirror
+    else if constexpr (D == 16)
+        return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+    else return __shfl_xor(v, 32);
+}
+// Value of lane (lane XOR D): a true exchange, for per-lane (not
+// group-uniform) data.
+template <int D>
+MOE_DEV float xor_lane(float v) {
+    if constexpr (D == 1) return dpp<0xB1>(v);
+    else if constexpr (D == 2) return dpp<0x4E>(v);
+    else if constexpr (D < 32)
+        return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (D << 10)));
+    else return __shfl_xor(v, 32);
+}
+
+template <int D>
+MOE_DEV int xstepi(int v) {
+    return __float_as_int(xstep<D>(__int_as_float(v)));
+}
+
+template <int S>
+MOE_DEV float seg_max(float v) {
+    if constexpr (S >= 2) v = fmaxf(v, xstep<1>(v));
+    if constexpr (S >= 4) v = fmaxf(v, xstep<2>(v));
+    if constexpr (S >= 8) v = fmaxf(v, xstep<4>(v));
+    if constexpr (S >= 16) v = fmaxf(v, xstep<8>(v));
+    if constexpr (S >= 32) v = fmaxf(v, xstep<16>(v));
+    if constexpr (S >= 64) v = fmaxf(v, xstep<32>(v));
+    return v;
+}
+
+template <int S>
+MOE_DEV float seg_sum(float v) {
+    if constexpr (S >= 2) v += xstep<1>(v);
+    if constexpr (S >= 4) v += xstep<2>(v);
+    if constexpr (S >= 8) v += xstep<4>(v);
+    if constexpr (S >= 16) v += xstep<8>(v);
+    if constexpr (S >= 32) v += xstep<16>(v);
+    if constexpr (S >= 64) v += xstep<32>(v);
+    return v;
+}
+
+template <int S>
+MOE_DEV int seg_sumi(int v) {
+    if constexpr (S >= 2) v += xstepi<1>(v);
+    if constexpr (S >= 4) v += xstepi<2>(v);
+    if constexpr (S >= 8) v += xstepi<4>(v);
+    if constexpr (S >= 16) v += xstepi<8>(v);
+    if constexpr (S >= 32) v += xstepi<16>(v);
+    if constexpr (S >= 64) v += xstepi<32>(v);
+    return v;
+}
+
+// Maximum over the whole wave of a value that is uniform inside each
+// segment of S lanes; the result is wave-uniform.
+template <int S>
+MOE_DEV int wave_max_over_segments(int v) {
+    if constexpr (S <= 1) v = max(v, xstepi<1>(v));
+    if constexpr (S <= 2) v = max(v, xstepi<2>(v));
+    if constexpr (S <= 4) v = max(v, xstepi<4>(v));
+    if constexpr (S <= 8) v = max(v, xstepi<8>(v));
+    if constexpr (S <= 16) v = max(v, xstepi<16>(v));
+    if constexpr (S <= 32) v = max(v, xstepi<32>(v));
+    return __builtin_amdgcn_readfirstlane(v);
+}
+
+// Inclusive prefix sum over the lanes of a segment (lane s gets the sum of
+// lanes 0..s of its segment): Hillis-Steele shifts inside 16-lane rows, then
+// the total of the preceding row(s) for segments wider than a row.
+template <int S>
+MOE_DEV int seg_incl_scan(int v, int s) {
+    if constexpr (S >= 2) { int t = dppi<0x111>(v); v += (s >= 1) ? t : 0; }   // row_shr:1
+    if constexpr (S >= 4) { int t = dppi<0x112>(v); v += (s >= 2) ? t : 0; }   // row_shr:2
+    if constexpr (S >= 8) { int t = dppi<0x114>(v); v += (s >= 4) ? t : 0; }   // row_shr:4
+    if constexpr (S >= 16) { int t = dppi<0x118>(v); v += (s >= 8) ? t : 0; }  // row_shr:8
+    if constexpr (S >= 32) {
+        const int lane = __lane_id();
+        int t = __shfl(v, (lane & ~31) | 15);
+        v += (s & 16) ? t : 0;
+    }
+    if constexpr (S >= 64) {
+        int t = __shfl(v, 31);
+        v += (s & 32) ? t : 0;
+    }
+    return v;
+}
+
+// Value held by another lane of the same segment; over R = 1..S-1 every
+// other lane of the segment is visited exactly once.
+template <int S, int R>
+MOE_DEV float seg_other(float v) {
+    static_assert(R >= 1 && R < S, "bad segment offset");
+    if constexpr (S == 2 || S == 4) {
+        // quad_perm with lane' = lane ^ R
+        constexpr int q0 = 0 ^ R, q1 = 1 ^ R, q2 = 2 ^ R, q3 = 3 ^ R;
+        return dpp<(q0 | (q1 << 2) | (q2 << 4) | (q3 << 6))>(v);
+    } else if constexpr (S == 16) {
+        return dpp<0x120 + R>(v);  // row_ror:R
+    } else if constexpr (S == 8 || S == 32) {
+        // swizzle, bit-mask mode: lane' = lane ^ R inside 32-lane groups
+        return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x1F | (R << 10)));
+    } else {
+        return __shfl_xor(v, R);
+    }
+}
+
+// Order key of (logit, expert): a larger key means "earlier in the top-k
+// order" -- larger logit, or equal logit and lower expert.  The logit is
+// canonicalised (-0.0 -> +0.0) and mapped to an order-preserving unsigned
+// integer in the high word; the low word is ~expert.
+MOE_DEV uint64_t make_key(float v, int col) {
+    uint32_t u = __float_as_uint(v + 0.0f);
+    uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    return (uint64_t(ord) << 32) | uint32_t(0xFFFFFFFFu - uint32_t(col));
+}
+MOE_DEV int key_col(uint64_t key) { return int(0xFFFFFFFFu - uint32_t(key)); }
+MOE_DEV float key_val(uint64_t key) {
+    uint32_t ord = uint32_t(key >> 32);
+    uint32_t u = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
+    return __uint_as_float(u);
+}
+
+MOE_DEV uint64_t shfl_xor_u64(uint64_t v, int m) {
+    int lo = __shfl_xor(int(uint32_t(v)), m);
+    int hi = __shfl_xor(int(uint32_t(v >> 32)), m);
+    return (uint64_t(uint32_t(hi)) << 32) | uint32_t(lo);
+}
+
+template <int S>
+MOE_DEV uint64_t seg_max_u64(uint64_t v) {
+#pragma unroll
+    for (int m = 1; m < S; m <<= 1) {
+        uint64_t o = shfl_xor_u64(v, m);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+MOE_DEV double shfl_xor_f64(double v, int m) {
+    uint64_t u = __double_as_longlong(v);
+    return __longlong_as_double((long long)shfl_xor_u64(u, m));
+}
+
+}  // namespace dev
+}  // namespace moe
