@@ -186,18 +186,25 @@ def main():
 
     # Let the host enqueue every timed step while the GPU is still busy, so
     # that the timed region measures the GPU and not the Python launch rate.
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    if hasattr(torch.cuda, "_sleep"):
-        torch.cuda._sleep(int(2e8))
-    t_start.record(stream)
-    h0 = time.perf_counter()
-    for i in range(K):
-        step(i, True)
-    host_s = time.perf_counter() - h0
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
+    def timed_loop(with_events):
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        if hasattr(torch.cuda, "_sleep"):
+            torch.cuda._sleep(int(2e8))
+        t0.record(stream)
+        h0 = time.perf_counter()
+        for i in range(K):
+            step(i, with_events)
+        hs = time.perf_counter() - h0
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1), hs
+
+    # 1) the step as a whole, nothing recorded between kernels
+    total_ms, host_s = timed_loop(False)
     ms_step = total_ms / K
+    # 2) the same steps with events around the dominant kernels
+    timed_loop(True)
     rows_ms = sum(hev.elapsed_ms(a, b) for a, b in ev_rows) / K
     bwd_ms = sum(hev.elapsed_ms(a, b) for a, b in ev_bwd) / K if w.backward else None
     status = int(out["status"].item())

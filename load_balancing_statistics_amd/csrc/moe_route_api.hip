@@ -1,6 +1,7 @@
 // moe_route_api.hip -- the C ABI declared in include/moe_route.h: argument
 // validation on the host, workspace sizing, and the launch sequence
-//   [gate transpose + gate GEMM] -> row pass -> block scan -> scatter/stats
+//   [gate transpose + gate GEMM] -> row pass -> block scan -> statistics
+//   -> dispatch scatter
 // for the forward, and the single streaming pass of the backward.
 #include <climits>
 #include <cmath>
@@ -42,10 +43,40 @@ int64_t capacity_of(const moe_route_params* p) {
 
 size_t workspace_bytes(const moe_route_params* p, const RowCfg& c) {
     const size_t gate = p->d > 0 ? moe::gate_workspace_bytes(p->d, p->E) : 0;
-    return moe::carve_workspace(nullptr, c.B, p->E, p->n_micro, gate).bytes;
+    return moe::carve_workspace(nullptr, c, p->E, p->n_micro, gate).bytes;
 }
 
 }  // namespace
+
+namespace moe {
+
+hipError_t launch_route_rows(const RowCfg& c, const RowsArgs& a, hipStream_t st) {
+    switch (c.S) {
+        case 1: return launch_rows_s<1>(c, a, st);
+        case 2: return launch_rows_s<2>(c, a, st);
+        case 4: return launch_rows_s<4>(c, a, st);
+        case 8: return launch_rows_s<8>(c, a, st);
+        case 16: return launch_rows_s<16>(c, a, st);
+        case 32: return launch_rows_s<32>(c, a, st);
+        case 64: return launch_rows_s<64>(c, a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_route_backward(const RowCfg& c, const BackArgs& a, hipStream_t st) {
+    switch (c.S) {
+        case 1: return launch_backward_s<1>(c, a, st);
+        case 2: return launch_backward_s<2>(c, a, st);
+        case 4: return launch_backward_s<4>(c, a, st);
+        case 8: return launch_backward_s<8>(c, a, st);
+        case 16: return launch_backward_s<16>(c, a, st);
+        case 32: return launch_backward_s<32>(c, a, st);
+        case 64: return launch_backward_s<64>(c, a, st);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace moe
 
 extern "C" {
 
@@ -93,7 +124,7 @@ int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
     const size_t need = workspace_bytes(p, c);
     if (!workspace || workspace_bytes_given < need || !aligned(workspace, 256)) return MOE_ERR_WORKSPACE;
     const moe::Workspace ws = moe::carve_workspace(
-        workspace, c.B, p->E, p->n_micro, gate ? moe::gate_workspace_bytes(p->d, p->E) : 0);
+        workspace, c, p->E, p->n_micro, gate ? moe::gate_workspace_bytes(p->d, p->E) : 0);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int Tm = p->T / p->n_micro;
 
@@ -109,6 +140,7 @@ int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
     ra.T = p->T; ra.E = p->E; ra.k = p->k; ra.Tm = Tm; ra.R = c.R; ra.bpm = c.bpm;
     ra.renorm = (p->flags & MOE_RENORM_TOPK) ? 1 : 0;
     ra.save_stats = (p->flags & MOE_SAVE_ROW_STATS) ? 1 : 0;
+    ra.qcap = moe::rows_queue_cap(c);
     ra.topk_idx = out->topk_idx; ra.topk_w = out->topk_w; ra.row_stats = out->row_stats;
     ra.cnt_part = ws.cnt_part; ra.P_part = ws.P_part; ra.flag_part = ws.flag_part;
     const bool timed = out->row_pass_events[0] && out->row_pass_events[1];
@@ -120,18 +152,28 @@ int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
 
     moe::ScanArgs sa{};
     sa.cnt_part = ws.cnt_part; sa.P_part = ws.P_part; sa.flag_part = ws.flag_part;
-    sa.E = p->E; sa.bpm = c.bpm; sa.n_micro = p->n_micro; sa.B = c.B;
-    sa.colprefix = ws.colprefix; sa.totals = ws.totals; sa.Psum = ws.Psum; sa.status = out->status;
+    sa.E = p->E; sa.bpm = c.bpm; sa.n_micro = p->n_micro; sa.B = c.B; sa.nsplit = c.nsplit;
+    sa.colprefix = ws.colprefix; sa.split_tot = ws.split_tot; sa.split_P = ws.split_P;
+    sa.status = out->status;
     if (moe::launch_route_scan(c, sa, st) != hipSuccess) return MOE_ERR_HIP;
 
+    moe::FinalArgs fa{};
+    fa.split_tot = ws.split_tot; fa.split_P = ws.split_P;
+    fa.E = p->E; fa.k = p->k; fa.Tm = Tm; fa.nsplit = c.nsplit;
+    fa.capacity = int(capacity_of(p)); fa.alpha = p->alpha;
+    fa.counts = out->counts; fa.offsets = out->offsets; fa.f = out->f; fa.P = out->P;
+    fa.aux = out->aux_loss; fa.cv = out->cv; fa.max_over_mean = out->max_over_mean;
+    fa.extra = out->extra_stats;
+    if (moe::launch_route_finalize(c, fa, p->n_micro, st) != hipSuccess) return MOE_ERR_HIP;
+
     moe::ScatterArgs ca{};
-    ca.topk_idx = out->topk_idx; ca.colprefix = ws.colprefix; ca.totals = ws.totals; ca.Psum = ws.Psum;
+    ca.topk_idx = out->topk_idx; ca.colprefix = ws.colprefix; ca.split_tot = ws.split_tot;
     ca.T = p->T; ca.E = p->E; ca.k = p->k; ca.Tm = Tm; ca.R = c.R; ca.bpm = c.bpm;
-    ca.capacity = int(capacity_of(p)); ca.alpha = p->alpha;
-    ca.counts = out->counts; ca.offsets = out->offsets; ca.perm = out->perm;
+    ca.nsplit = c.nsplit;
+    ca.capacity = int(capacity_of(p));
+    ca.perm = out->perm;
     ca.inv_perm = (p->flags & MOE_WRITE_INV_PERM) ? out->inv_perm : nullptr;
-    ca.dropped = out->dropped; ca.f = out->f; ca.P = out->P; ca.aux = out->aux_loss; ca.cv = out->cv;
-    ca.max_over_mean = out->max_over_mean; ca.extra = out->extra_stats; ca.status = out->status;
+    ca.dropped = out->dropped; ca.status = out->status;
     if (moe::launch_route_scatter(c, ca, st) != hipSuccess) return MOE_ERR_HIP;
     return MOE_OK;
 }

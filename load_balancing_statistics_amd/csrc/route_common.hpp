@@ -16,17 +16,24 @@ namespace moe {
 
 // ----------------------------------------------------------------- config
 struct RowCfg {
-    int S;      // lanes per row (power of two, >= k)
-    int G;      // columns per lane
-    int NW;     // waves per block
-    int R;      // rows per block
-    int bpm;    // blocks per microbatch
-    int B;      // blocks in total (= n_micro * bpm)
+    int S;       // lanes per row (power of two, >= k)
+    int G;       // columns per lane
+    int VEC;     // floats per load: 4 when E % 4 == 0, else 1
+    int PAD;     // 1 when S*G > E (some lane columns fall past the row)
+    int NW;      // waves per block
+    int R;       // rows of the largest block (blocks differ by at most one row)
+    int bpm;     // row blocks per microbatch
+    int B;       // row blocks in total (= n_micro * bpm)
+    int nsplit;  // block-scan splits per microbatch
 };
 
-// Column counts per lane that have kernel instantiations.
-constexpr int kGTable[] = {1, 2, 4, 8, 12, 16, 24};
+// Columns per lane that have kernel instantiations.
+constexpr int kGTableVec4[] = {4, 8, 16, 24};
+constexpr int kGTableVec1[] = {1, 2, 4, 8, 16, 24};
 constexpr int kGMax = 24;
+constexpr int kScanWaves = 16;     // waves per block-scan block
+constexpr int kScanPerWave = 8;    // row blocks per block-scan wave
+constexpr int kAssumedCUs = 256;   // MI355X compute units (grid sizing only)
 
 inline int next_pow2(int v) {
     int p = 1;
@@ -34,34 +41,54 @@ inline int next_pow2(int v) {
     return p;
 }
 
-inline int round_g(int g) {
-    for (int t : kGTable)
-        if (g <= t) return t;
-    return -1;
-}
-
 // Pick the lane mapping: the narrowest segment (S >= k, power of two) whose
-// per-lane column count fits the table; then rows per block so that large
-// workloads launch on the order of a thousand blocks.
+// per-lane column count fits the table.  Then the rows per block: about two
+// or three resident blocks per compute unit over the whole batch, so the
+// grid is one wave of blocks and the per-block partials stay few.
 inline RowCfg choose_rows(int T, int E, int k, int n_micro) {
     RowCfg c{};
+    c.VEC = (E % 4 == 0) ? 4 : 1;
     int S = next_pow2(k < 1 ? 1 : k);
     while (S < 64 && (E + S - 1) / S > kGMax) S <<= 1;
     c.S = S;
-    c.G = round_g((E + S - 1) / S);
-    c.NW = 8;
+    const int g0 = (E + S - 1) / S;
+    c.G = -1;
+    if (c.VEC == 4) {
+        for (int t : kGTableVec4) if (c.G < 0 && g0 <= t) c.G = t;
+    } else {
+        for (int t : kGTableVec1) if (c.G < 0 && g0 <= t) c.G = t;
+    }
+    // unaligned rows take the generic (bounds-checked) column path
+    c.PAD = (S * c.G != E || c.VEC == 1) ? 1 : 0;
+    // One block per compute unit holding as many waves as the row pass's
+    // registers allow: 16 (4 per SIMD) when a lane owns up to 16 columns,
+    // 12 when it owns 24.
+    c.NW = (c.G > 16) ? 12 : 16;
     const int W = 64 / S;
-    const int per_iter = c.NW * W;
+    const long per_iter = long(c.NW) * W;
     const long Tm = T / n_micro;
-    long iters = (long(T) + per_iter * 1024L - 1) / (per_iter * 1024L);
-    if (iters < 1) iters = 1;
-    if (iters > 16) iters = 16;
-    long R = per_iter * iters;
-    if (R > Tm) R = ((Tm + per_iter - 1) / per_iter) * per_iter;
-    c.R = int(R);
-    c.bpm = int((Tm + R - 1) / R);
+    const long blocks_per_cu = 1;
+    const long target = kAssumedCUs * blocks_per_cu;
+    // balanced split: every block of a microbatch gets floor or ceil of
+    // Tm / bpm rows, at least one row group per wave iteration
+    long bpm = (target + n_micro - 1) / n_micro;
+    const long max_bpm = (Tm + per_iter - 1) / per_iter;
+    if (bpm > max_bpm) bpm = max_bpm;
+    if (bpm < 1) bpm = 1;
+    c.bpm = int(bpm);
+    c.R = int((Tm + bpm - 1) / bpm);  // rows of the largest block
     c.B = c.bpm * n_micro;
+    const int per_split = kScanWaves * kScanPerWave;
+    c.nsplit = (c.bpm + per_split - 1) / per_split;
     return c;
+}
+
+// Rows [begin, end) of row block b: microbatch b / bpm, balanced split of
+// its Tm rows over bpm blocks.
+__host__ __device__ inline void block_rows(int b, int bpm, int Tm, long& begin, long& end) {
+    const int mb = b / bpm, bi = b - (b / bpm) * bpm;
+    begin = long(mb) * Tm + (long(bi) * Tm) / bpm;
+    end = long(mb) * Tm + (long(bi + 1) * Tm) / bpm;
 }
 
 // Candidate-list capacity per row for the threshold top-k (see route_rows).
@@ -69,34 +96,48 @@ __host__ __device__ constexpr int cand_cap(int S, int G) {
     return (S * G < (2 * S > 32 ? 2 * S : 32)) ? S * G : (2 * S > 32 ? 2 * S : 32);
 }
 
+// Candidate-list row stride (keys): room for the list padded to a multiple of
+// 4 keys (read 4 at a time), plus 2 so that rows start 16-byte aligned on
+// different banks.
+__host__ __device__ constexpr int cand_stride(int S, int G) { return ((cand_cap(S, G) + 3) & ~3) + 2; }
+
 // LDS row stride (floats) of the row copy: S times an odd number >= G, so
 // the segments of a wave start on distinct banks.
 __host__ __device__ constexpr int row_stride(int S, int G) { return S * (G | 1); }
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// Per-wave capacity of the overflow queue of the row pass: one entry for
+// every row the wave can process.
+inline int rows_queue_cap(const RowCfg& c) {
+    const int W = 64 / c.S;
+    const int per_iter = c.NW * W;
+    return ((c.R + per_iter - 1) / per_iter) * W;
+}
+
 inline size_t rows_lds_bytes(const RowCfg& c, int E, int k) {
     const int W = 64 / c.S;
     size_t hist = align_up(size_t(E) * 4, 16);
     size_t rowbuf = size_t(c.NW) * W * row_stride(c.S, c.G) * 4;
-    size_t cand = size_t(c.NW) * W * (cand_cap(c.S, c.G) + 1) * 8;
+    size_t cand = size_t(c.NW) * W * cand_stride(c.S, c.G) * 8;
     size_t sel = size_t(c.NW) * W * k * 8;
-    return hist + align_up(rowbuf, 16) + cand + sel;
+    size_t queue = size_t(c.NW) * rows_queue_cap(c) * 4;
+    return hist + align_up(rowbuf, 16) + cand + sel + queue;
 }
 
 // Workspace carve-up (each piece 256-byte aligned).
 struct Workspace {
-    int32_t* cnt_part;    // [B,E]   per-block histograms
-    float*   P_part;      // [B,E]   per-block probability sums
-    int32_t* flag_part;   // [B]     per-block status bits
-    int32_t* colprefix;   // [B,E]   exclusive prefix over blocks of the microbatch
-    int32_t* totals;      // [m,E]   counts per microbatch
-    double*  Psum;        // [m,E]   probability sums per microbatch
-    uint16_t* Wt;         // [E,d]   transposed gate weights (gate path only)
+    int32_t* cnt_part;    // [B,E]        per-block histograms
+    float*   P_part;      // [B,E]        per-block probability sums
+    int32_t* flag_part;   // [B]          per-block status bits
+    int32_t* colprefix;   // [B,E]        exclusive prefix over the blocks of a split
+    int32_t* split_tot;   // [m,nsplit,E] counts per split
+    double*  split_P;     // [m,nsplit,E] probability sums per split
+    uint16_t* Wt;         // [E,d]        transposed gate weights (gate path only)
     size_t   bytes;
 };
 
-inline Workspace carve_workspace(void* base, int B, int E, int m, size_t gate_bytes) {
+inline Workspace carve_workspace(void* base, const RowCfg& c, int E, int m, size_t gate_bytes) {
     Workspace w{};
     size_t off = 0;
     auto take = [&](size_t n) {
@@ -104,12 +145,13 @@ inline Workspace carve_workspace(void* base, int B, int E, int m, size_t gate_by
         off = align_up(off + n, 256);
         return o;
     };
-    size_t o_cnt = take(size_t(B) * E * 4);
-    size_t o_P = take(size_t(B) * E * 4);
-    size_t o_flag = take(size_t(B) * 4);
-    size_t o_pre = take(size_t(B) * E * 4);
-    size_t o_tot = take(size_t(m) * E * 4);
-    size_t o_ps = take(size_t(m) * E * 8);
+    const size_t B = size_t(c.B), ns = size_t(c.nsplit);
+    size_t o_cnt = take(B * E * 4);
+    size_t o_P = take(B * E * 4);
+    size_t o_flag = take(B * 4);
+    size_t o_pre = take(B * E * 4);
+    size_t o_tot = take(size_t(m) * ns * E * 4);
+    size_t o_ps = take(size_t(m) * ns * E * 8);
     size_t o_wt = take(gate_bytes);
     w.bytes = off;
     char* b = static_cast<char*>(base);
@@ -118,8 +160,8 @@ inline Workspace carve_workspace(void* base, int B, int E, int m, size_t gate_by
         w.P_part = reinterpret_cast<float*>(b + o_P);
         w.flag_part = reinterpret_cast<int32_t*>(b + o_flag);
         w.colprefix = reinterpret_cast<int32_t*>(b + o_pre);
-        w.totals = reinterpret_cast<int32_t*>(b + o_tot);
-        w.Psum = reinterpret_cast<double*>(b + o_ps);
+        w.split_tot = reinterpret_cast<int32_t*>(b + o_tot);
+        w.split_P = reinterpret_cast<double*>(b + o_ps);
         w.Wt = gate_bytes ? reinterpret_cast<uint16_t*>(b + o_wt) : nullptr;
     }
     return w;
@@ -130,6 +172,7 @@ struct RowsArgs {
     const float* logits;
     int T, E, k, Tm, R, bpm;
     int renorm, save_stats;
+    int qcap;  // per-wave queue entries: row groups of the largest block times rows per group
     int32_t* topk_idx;
     float* topk_w;
     float* row_stats;
@@ -142,33 +185,39 @@ struct ScanArgs {
     const int32_t* cnt_part;
     const float* P_part;
     const int32_t* flag_part;
-    int E, bpm, n_micro, B;
+    int E, bpm, n_micro, B, nsplit;
     int32_t* colprefix;
-    int32_t* totals;
-    double* Psum;
+    int32_t* split_tot;
+    double* split_P;
     int32_t* status;
 };
 
 struct ScatterArgs {
     const int32_t* topk_idx;
     const int32_t* colprefix;
-    const int32_t* totals;
-    const double* Psum;
-    int T, E, k, Tm, R, bpm;
+    const int32_t* split_tot;
+    int T, E, k, Tm, R, bpm, nsplit;
+    int capacity;  // < 0: unlimited
+    int32_t* perm;
+    int32_t* inv_perm;
+    uint8_t* dropped;
+    int32_t* status;
+};
+
+struct FinalArgs {
+    const int32_t* split_tot;
+    const double* split_P;
+    int E, k, Tm, nsplit;
     int capacity;  // < 0: unlimited
     float alpha;
     int32_t* counts;
     int32_t* offsets;
-    int32_t* perm;
-    int32_t* inv_perm;
-    uint8_t* dropped;
     float* f;
     float* P;
     float* aux;
     float* cv;
     float* max_over_mean;
     float* extra;
-    int32_t* status;
 };
 
 struct BackArgs {
@@ -190,8 +239,19 @@ struct GateArgs {
 
 // Launchers (each defined next to its kernel).  Return a hipError_t.
 hipError_t launch_route_rows(const RowCfg& c, const RowsArgs& a, hipStream_t st);
+template <int S>
+hipError_t launch_rows_s(const RowCfg& c, const RowsArgs& a, hipStream_t st);
+template <int S>
+hipError_t launch_backward_s(const RowCfg& c, const BackArgs& a, hipStream_t st);
+#define MOE_DECLARE_SEGMENT(SV)                                                           \
+    template <> hipError_t launch_rows_s<SV>(const RowCfg&, const RowsArgs&, hipStream_t); \
+    template <> hipError_t launch_backward_s<SV>(const RowCfg&, const BackArgs&, hipStream_t);
+MOE_DECLARE_SEGMENT(1) MOE_DECLARE_SEGMENT(2) MOE_DECLARE_SEGMENT(4) MOE_DECLARE_SEGMENT(8)
+MOE_DECLARE_SEGMENT(16) MOE_DECLARE_SEGMENT(32) MOE_DECLARE_SEGMENT(64)
+#undef MOE_DECLARE_SEGMENT
 hipError_t launch_route_scan(const RowCfg& c, const ScanArgs& a, hipStream_t st);
 hipError_t launch_route_scatter(const RowCfg& c, const ScatterArgs& a, hipStream_t st);
+hipError_t launch_route_finalize(const RowCfg& c, const FinalArgs& a, int n_micro, hipStream_t st);
 hipError_t launch_route_backward(const RowCfg& c, const BackArgs& a, hipStream_t st);
 hipError_t launch_gate_gemm(const GateArgs& a, uint16_t* wt, hipStream_t st);
 bool gate_supported(int T, int d, int E);
@@ -211,14 +271,18 @@ namespace dev {
 
 constexpr float kLog2e = 1.4426950408889634f;
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 // DPP move with a compile-time control word (row/bank masks full).
+// DPP move with a compile-time control word (row/bank masks full; lanes with
+// no source read 0), foldable into the instruction that consumes it.
 template <int CTRL>
 MOE_DEV float dpp(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 template <int CTRL>
 MOE_DEV int dppi(int v) {
-    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
 }
 
 // Partner value for a butterfly step of distance D inside aligned groups of
@@ -302,10 +366,17 @@ MOE_DEV int wave_max_over_segments(int v) {
 // the total of the preceding row(s) for segments wider than a row.
 template <int S>
 MOE_DEV int seg_incl_scan(int v, int s) {
-    if constexpr (S >= 2) { int t = dppi<0x111>(v); v += (s >= 1) ? t : 0; }   // row_shr:1
-    if constexpr (S >= 4) { int t = dppi<0x112>(v); v += (s >= 2) ? t : 0; }   // row_shr:2
-    if constexpr (S >= 8) { int t = dppi<0x114>(v); v += (s >= 4) ? t : 0; }   // row_shr:4
-    if constexpr (S >= 16) { int t = dppi<0x118>(v); v += (s >= 8) ? t : 0; }  // row_shr:8
+    if constexpr (S >= 16) {
+        // segments are whole rows: lanes shifted in from before the row read 0
+        v += dppi<0x111>(v);  // row_shr:1
+        v += dppi<0x112>(v);  // row_shr:2
+        v += dppi<0x114>(v);  // row_shr:4
+        v += dppi<0x118>(v);  // row_shr:8
+    } else {
+        if constexpr (S >= 2) { int t = dppi<0x111>(v); v += (s >= 1) ? t : 0; }
+        if constexpr (S >= 4) { int t = dppi<0x112>(v); v += (s >= 2) ? t : 0; }
+        if constexpr (S >= 8) { int t = dppi<0x114>(v); v += (s >= 4) ? t : 0; }
+    }
     if constexpr (S >= 32) {
         const int lane = __lane_id();
         int t = __shfl(v, (lane & ~31) | 15);

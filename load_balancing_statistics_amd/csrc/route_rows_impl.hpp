@@ -1,0 +1,575 @@
+// route_rows_impl.hpp -- kernel templates of the two per-token streaming
+// passes: the forward row pass and the aux-loss backward.  Instantiated per
+// segment width S by route_s<S>.hip.
+//
+// Forward row pass.  For every token (row of logits [T,E]) one streaming read
+// produces:
+//   * the softmax statistics m = max_e l, s = sum_e exp(l - m)
+//     (page mhpq.cn/news/998159 section 4.2: the router probabilities are a
+//     softmax over the experts);
+//   * the top-k experts in (logit desc, expert asc) order and their gate
+//     weights (section 4.4 of that page: every token is dispatched to k
+//     experts), optionally renormalised over the k picks;
+//   * the block's expert histogram (LDS integer atomics) and the block's
+//     per-expert sums of softmax probabilities, used for f_i and P_i.
+//
+// Top-k without sorting.  Lane s of a segment owns G columns.  The k-th
+// largest of the S lane maxima, tau, is a lower bound of the row's k-th
+// largest logit (k lanes each hold a value >= tau), so the logits >= tau
+// contain the top k.  For the routing workloads that is about 7-10 of 256-384
+// logits; they are compacted into LDS as 64-bit order keys and ranked by
+// counting, which yields the exact top-k with ties to the lower expert.  A
+// row with more candidates than the list holds (massive ties) takes an exact
+// k-round arg-max over its logits instead.
+//
+// Backward.  L_aux = alpha*E*sum_i f_i*P_i with f a constant observation
+// (pages mhpq.cn/news/998159 section 4.2 and codechina.net article 413310
+// section 2.2: the gradient reaches the router through P only):
+//   dL/dl[t,j] = g_mb * alpha * E / Tm * p[t,j] * (f_j - sum_i f_i p[t,i]).
+//
+// Layout: lane s of a segment owns the columns VEC*(j*S + s) + v, j < G/VEC,
+// v < VEC, so each vector load of a segment reads S*VEC consecutive floats.
+// Determinism: integer histogram; every float sum has a fixed order.
+#pragma once
+
+#include "route_common.hpp"
+
+namespace moe {
+namespace rows_impl {
+
+using namespace dev;
+
+// 1 + the number of other lanes of the segment whose maximum is >= lmax.
+template <int S, int R>
+__device__ __forceinline__ int count_ge(float lmax) {
+    if constexpr (R >= S) {
+        return 1;
+    } else {
+        return ((seg_other<S, R>(lmax) >= lmax) ? 1 : 0) + count_ge<S, R + 1>(lmax);
+    }
+}
+
+template <int S, int VEC>
+__device__ __forceinline__ int col_of(int g, int s) {
+    return VEC * ((g / VEC) * S + s) + (g % VEC);
+}
+
+// Load the G owned logits of a row.  The row index is clamped into the
+// block's range and padding columns are clamped to the row, so every load is
+// in bounds and unconditional; padding values become -inf.
+template <int S, int G, int VEC, bool PAD>
+__device__ __forceinline__ void load_row(float (&x)[G], const float* __restrict__ logits,
+                                         long row, int E, int s) {
+    const float* src = logits + row * E;
+    if constexpr (VEC == 4) {
+#pragma unroll
+        for (int j = 0; j < G / 4; ++j) {
+            int c0 = 4 * (j * S + s);
+            const bool in = !PAD || c0 < E;
+            if constexpr (PAD) c0 = in ? c0 : E - 4;
+            const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + c0));
+            x[4 * j + 0] = in ? v[0] : -INFINITY;
+            x[4 * j + 1] = in ? v[1] : -INFINITY;
+            x[4 * j + 2] = in ? v[2] : -INFINITY;
+            x[4 * j + 3] = in ? v[3] : -INFINITY;
+        }
+    } else {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            int c = g * S + s;
+            const bool in = !PAD || c < E;
+            if constexpr (PAD) c = in ? c : E - 1;
+            const float v = __builtin_nontemporal_load(src + c);
+            x[g] = in ? v : -INFINITY;
+        }
+    }
+}
+
+template <int S, int G, int VEC, bool PAD, int NW>
+struct RowPass {
+    static constexpr int W = 64 / S;               // rows per wave at a time
+    static constexpr int RS = row_stride(S, G);    // LDS row-copy stride (floats)
+    static constexpr int CAP = cand_cap(S, G);     // candidate list capacity
+    static constexpr int CS = cand_stride(S, G);   // candidate row stride (keys)
+    static constexpr int NP = (CAP + S - 1) / S;   // ranking passes at most
+
+    // Exact top-k of a row from its LDS copy: k rounds of arg-max of the
+    // order keys over the segment (rows whose candidate list overflows).
+    __device__ __forceinline__ static void fallback_select(
+        const float* rowbuf, uint64_t* sel, int E, int k, int s) {
+        uint64_t prev = ~0ull;
+        for (int j = 0; j < k; ++j) {
+            uint64_t best = 0;
+            for (int g = 0; g < G; ++g) {
+                const int col = col_of<S, VEC>(g, s);
+                if (!PAD || col < E) {
+                    const uint64_t key = make_key(rowbuf[col], col);
+                    if (key < prev && key > best) best = key;
+                }
+            }
+            best = seg_max_u64<S>(best);
+            if (s == 0) sel[j] = best;
+            prev = best;
+        }
+    }
+
+    __device__ __forceinline__ static int col_from_bit(int g, int s) {
+        return (VEC == 4) ? (4 * ((g >> 2) * S + s) + (g & 3)) : (g * S + s);
+    }
+
+    // One row (per segment): everything the forward needs from it.
+    //
+    // LDS traffic is arranged so that no step waits on a fresh round trip
+    // more than necessary: the row copy is written and the lane's first
+    // candidates are read back before the softmax arithmetic, which hides
+    // the read latency; candidates then rank themselves against the whole
+    // list (one batch of reads) and the winners write the outputs directly.
+    __device__ __forceinline__ static void process(
+        const RowsArgs& a, const float (&x)[G], long row, bool valid, int s,
+        float* rowbuf, uint64_t* cand, int* hist, float (&acc)[G], int& bad,
+        int* queue, int& qn, long row_begin)
+    {
+        const int E = a.E, k = a.k;
+        // ---- row maximum and the candidate threshold tau
+        float lmax = x[0];
+#pragma unroll
+        for (int g = 1; g < G; ++g) lmax = fmaxf(lmax, x[g]);
+        const float m = seg_max<S>(lmax);
+        float tau = m;
+        if constexpr (S > 1) {
+            if (k > 1) {
+                const int ge = count_ge<S, 1>(lmax);
+                // the largest lane maximum reached by at least k lane maxima
+                tau = seg_max<S>(ge >= k ? lmax : -INFINITY);
+            }
+        }
+
+        // ---- candidates x >= tau (bit g of mask), real columns only
+        unsigned mask = 0;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const bool real = !PAD || col_of<S, VEC>(g, s) < E;
+            mask |= (x[g] >= tau && real) ? (1u << g) : 0u;
+        }
+        if (!valid) mask = 0;
+        const int n = __popc(mask);
+        const int incl = seg_incl_scan<S>(n, s);
+        const int C = seg_sumi<S>(n);
+
+        // ---- row copy (LDS), then read back this lane's first candidates
+        if constexpr (VEC == 4) {
+#pragma unroll
+            for (int j = 0; j < G / 4; ++j)
+                *reinterpret_cast<f32x4*>(rowbuf + 4 * (j * S + s)) =
+                    f32x4{x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]};
+        } else {
+#pragma unroll
+            for (int g = 0; g < G; ++g) rowbuf[g * S + s] = x[g];
+        }
+        constexpr int XB = 4;  // candidates extracted per lane up front
+        unsigned mm = mask;
+        int ecol[XB];
+        float ev[XB];
+#pragma unroll
+        for (int u = 0; u < XB; ++u) {
+            const int g = mm ? __ffs(mm) - 1 : 0;
+            mm &= mm - 1;
+            ecol[u] = col_from_bit(g, s);
+        }
+#pragma unroll
+        for (int u = 0; u < XB; ++u) ev[u] = rowbuf[ecol[u]];
+
+        // ---- softmax statistics and probability sums (hides the reads)
+        const float mL = m * kLog2e;
+        float ex[G];
+        float ssum = 0.f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            ex[g] = __builtin_amdgcn_exp2f(fmaf(x[g], kLog2e, -mL));
+            ssum += ex[g];
+        }
+        ssum = seg_sum<S>(ssum);
+        const float inv = __builtin_amdgcn_rcpf(ssum);
+        if (valid) {
+#pragma unroll
+            for (int g = 0; g < G; ++g) acc[g] = fmaf(ex[g], inv, acc[g]);
+            if (!(ssum > 0.f && ssum <= 3.0e38f)) bad = 1;
+        }
+
+        // ---- exact top-k: winners as (rank, expert, exp) per ranking pass
+        int wrank[NP], wcol[NP];
+        float we[NP];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) wrank[p] = -1;
+
+        // Rows whose candidate list would overflow (massive ties) are queued
+        // and resolved after the streaming loop; the rest rank here.
+        const bool need_fb = valid && (C > CAP || C < k);
+        const uint64_t fbmask = __ballot(need_fb && s == 0);
+        if (__builtin_expect(fbmask != 0, 0)) {
+            if (need_fb && s == 0) {
+                const uint64_t lt = (__lane_id() == 0) ? 0ull : (~0ull >> (64 - __lane_id()));
+                queue[qn + __popcll(fbmask & lt)] = int(row - row_begin);
+            }
+            qn += __popcll(fbmask);
+        }
+        if (!need_fb) {
+            // compact the candidates' order keys into the row's list
+            const int o = incl - n;
+#pragma unroll
+            for (int u = 0; u < XB; ++u)
+                if (u < n) cand[o + u] = make_key(ev[u], ecol[u]);
+            if (__builtin_expect(__any(n > XB), 0)) {
+                int o2 = o + XB;
+                while (mm) {
+                    const int g = __ffs(mm) - 1;
+                    mm &= mm - 1;
+                    const int col = col_from_bit(g, s);
+                    cand[o2++] = make_key(rowbuf[col], col);
+                }
+            }
+            // pad the list to a multiple of 4 keys
+            const int C4 = (C + 3) & ~3;
+            for (int p = C + s; p < C4; p += S) cand[p] = 0ull;
+            // candidate c ranks itself against the whole list
+            const ulonglong2* cand2 = reinterpret_cast<const ulonglong2*>(cand);
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                const int c = p * S + s;
+                if (p * S < C) {
+                    const uint64_t my = (c < C) ? cand[c] : 0ull;
+                    int rank = 0;
+                    for (int c2 = 0; c2 < C4; c2 += 4) {
+                        const ulonglong2 k01 = cand2[c2 / 2];
+                        const ulonglong2 k23 = cand2[c2 / 2 + 1];
+                        rank += (k01.x > my) ? 1 : 0;
+                        rank += (k01.y > my) ? 1 : 0;
+                        rank += (k23.x > my) ? 1 : 0;
+                        rank += (k23.y > my) ? 1 : 0;
+                    }
+                    if (c < C && rank < k) {
+                        wrank[p] = rank;
+                        wcol[p] = key_col(my);
+                        we[p] = __builtin_amdgcn_exp2f(fmaf(key_val(my), kLog2e, -mL));
+                    }
+                }
+            }
+        }
+
+        // ---- gate weights, outputs, histogram
+        float esum = 0.f;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) esum += (wrank[p] >= 0) ? we[p] : 0.f;
+        const float rden = a.renorm ? __builtin_amdgcn_rcpf(seg_sum<S>(esum)) : inv;
+        if (valid) {
+#pragma unroll
+            for (int p = 0; p < NP; ++p) {
+                if (wrank[p] >= 0) {
+                    a.topk_idx[row * k + wrank[p]] = wcol[p];
+                    a.topk_w[row * k + wrank[p]] = we[p] * rden;
+                    atomicAdd(&hist[wcol[p]], 1);
+                }
+            }
+            if (s == 0 && a.save_stats) {
+                a.row_stats[2 * row] = m;
+                a.row_stats[2 * row + 1] = ssum;
+            }
+        }
+    }
+
+    // Queued rows (candidate-list overflow): reload, softmax statistics, exact
+    // top-k by k rounds of arg-max, outputs.  Probability sums were already
+    // accumulated by the streaming pass.
+    __device__ __forceinline__ static void resolve_queue(
+        const RowsArgs& a, const int* queue, int qn, long row_begin, int s, int seg,
+        float* rowbuf, uint64_t* sel, int* hist)
+    {
+        const int E = a.E, k = a.k;
+        for (int q0 = 0; q0 < qn; q0 += W) {
+            const bool has = q0 + seg < qn;
+            const long row = row_begin + (has ? queue[q0 + seg] : queue[q0]);
+            float x[G];
+            load_row<S, G, VEC, PAD>(x, a.logits, row, E, s);
+            float lmax = x[0];
+#pragma unroll
+            for (int g = 1; g < G; ++g) lmax = fmaxf(lmax, x[g]);
+            const float m = seg_max<S>(lmax);
+            const float mL = m * kLog2e;
+            float ssum = 0.f;
+#pragma unroll
+            for (int g = 0; g < G; ++g) ssum += __builtin_amdgcn_exp2f(fmaf(x[g], kLog2e, -mL));
+            ssum = seg_sum<S>(ssum);
+#pragma unroll
+            for (int g = 0; g < G; ++g) rowbuf[col_of<S, VEC>(g, s)] = x[g];
+            fallback_select(rowbuf, sel, E, k, s);
+            float e = 0.f;
+            int col = 0;
+            if (s < k) {
+                const uint64_t key = sel[s];
+                col = key_col(key);
+                e = __builtin_amdgcn_exp2f(fmaf(key_val(key), kLog2e, -mL));
+            }
+            const float rden = a.renorm ? __builtin_amdgcn_rcpf(seg_sum<S>(s < k ? e : 0.f))
+                                        : __builtin_amdgcn_rcpf(ssum);
+            if (has && s < k) {
+                a.topk_idx[row * k + s] = col;
+                a.topk_w[row * k + s] = e * rden;
+                atomicAdd(&hist[col], 1);
+            }
+        }
+    }
+};
+
+template <int S, int G, int VEC, bool PAD, int NW>
+__global__ void __launch_bounds__(NW * 64)
+route_rows_kernel(const RowsArgs a)
+{
+    using RP = RowPass<S, G, VEC, PAD, NW>;
+    constexpr int W = RP::W, RS = RP::RS, CS = RP::CS;
+
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int E = a.E, k = a.k;
+    int* hist = reinterpret_cast<int*>(smem);
+    float* rowbuf_all = reinterpret_cast<float*>(smem + ((E * 4 + 15) & ~15));
+    uint64_t* cand_all = reinterpret_cast<uint64_t*>(
+        reinterpret_cast<unsigned char*>(rowbuf_all) + ((NW * W * RS * 4 + 15) & ~15));
+    uint64_t* sel_all = cand_all + NW * W * CS;
+    int* queue_all = reinterpret_cast<int*>(sel_all + NW * W * k);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int seg = lane / S, s = lane % S;
+    long row_begin, row_end;
+    block_rows(blockIdx.x, a.bpm, a.Tm, row_begin, row_end);
+
+    for (int e = tid; e < E; e += NW * 64) hist[e] = 0;
+    __syncthreads();
+
+    float* rowbuf = rowbuf_all + (wave * W + seg) * RS;
+    uint64_t* cand = cand_all + (wave * W + seg) * CS;
+    uint64_t* sel = sel_all + (wave * W + seg) * k;
+    int* queue = queue_all + wave * a.qcap;
+    int qn = 0;
+
+    float acc[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) acc[g] = 0.f;
+    int bad = 0;
+
+    const long per_iter = long(NW) * W;
+    const int iters = int((row_end - row_begin + per_iter - 1) / per_iter);
+    const long row0 = row_begin + long(wave) * W + seg;
+    auto row_at = [&](int it) { return row0 + long(it) * per_iter; };
+    auto clamp = [&](long r) { return r < row_end ? r : row_end - 1; };
+
+    // Two register buffers: load the next row group while processing one.
+    // Inside the loop every prefetch is unconditional (clamped rows), so the
+    // wait before processing a buffer covers only that buffer's loads.
+    float xa[G], xb[G];
+    load_row<S, G, VEC, PAD>(xa, a.logits, clamp(row_at(0)), E, s);
+    int it = 0;
+    for (; it + 2 < iters; it += 2) {
+        load_row<S, G, VEC, PAD>(xb, a.logits, clamp(row_at(it + 1)), E, s);
+        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin);
+        load_row<S, G, VEC, PAD>(xa, a.logits, clamp(row_at(it + 2)), E, s);
+        RP::process(a, xb, row_at(it + 1), row_at(it + 1) < row_end, s, rowbuf, cand, hist,
+                    acc, bad, queue, qn, row_begin);
+    }
+    if (it + 1 < iters) {
+        load_row<S, G, VEC, PAD>(xb, a.logits, clamp(row_at(it + 1)), E, s);
+        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin);
+        RP::process(a, xb, row_at(it + 1), row_at(it + 1) < row_end, s, rowbuf, cand, hist,
+                    acc, bad, queue, qn, row_begin);
+    } else if (it < iters) {
+        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin);
+    }
+
+    if (__builtin_expect(qn > 0, 0))
+        RP::resolve_queue(a, queue, qn, row_begin, s, seg, rowbuf, sel, hist);
+
+    // ---- block partials: probability sums (fixed order) and histogram.
+    // Lanes with the same s in different segments own the same columns.
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        if constexpr (S <= 1) acc[g] += xor_lane<1>(acc[g]);
+        if constexpr (S <= 2) acc[g] += xor_lane<2>(acc[g]);
+        if constexpr (S <= 4) acc[g] += xor_lane<4>(acc[g]);
+        if constexpr (S <= 8) acc[g] += xor_lane<8>(acc[g]);
+        if constexpr (S <= 16) acc[g] += xor_lane<16>(acc[g]);
+        if constexpr (S <= 32) acc[g] += xor_lane<32>(acc[g]);
+    }
+    const int any_bad = __syncthreads_or(bad);
+    float* pbuf = rowbuf_all;  // reused: [NW][E]
+    if (seg == 0) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int col = col_of<S, VEC>(g, s);
+            if (!PAD || col < E) pbuf[wave * E + col] = acc[g];
+        }
+    }
+    __syncthreads();
+    const long bo = long(blockIdx.x) * E;
+    for (int e = tid; e < E; e += NW * 64) {
+        float t = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) t += pbuf[w * E + e];
+        a.P_part[bo + e] = t;
+        a.cnt_part[bo + e] = hist[e];
+    }
+    if (tid == 0) a.flag_part[blockIdx.x] = any_bad ? MOE_STATUS_NONFINITE : 0;
+}
+
+template <int S, int G, int VEC, bool PAD, int NW>
+__global__ void __launch_bounds__(NW * 64)
+route_backward_kernel(const BackArgs a)
+{
+    constexpr int W = 64 / S;
+    const int E = a.E;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int seg = lane / S, s = lane % S;
+    const int mb = blockIdx.x / a.bpm;
+    long row_begin, row_end;
+    block_rows(blockIdx.x, a.bpm, a.Tm, row_begin, row_end);
+
+    const float inv_total = 1.0f / (float(a.Tm) * float(a.k));
+    float fcol[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+        const int col = col_of<S, VEC>(g, s);
+        fcol[g] = (!PAD || col < E) ? float(a.counts[long(mb) * E + col]) * inv_total : 0.f;
+    }
+    const float gup = a.d_aux ? a.d_aux[mb] : 1.0f;
+    const float c = gup * a.alpha * float(E) / float(a.Tm);
+
+    const long per_iter = long(NW) * W;
+    for (long row = row_begin + long(wave) * W + seg; row - seg < row_end; row += per_iter) {
+        const bool valid = row < row_end;
+        const long lr = valid ? row : row_end - 1;
+        float x[G];
+        load_row<S, G, VEC, PAD>(x, a.logits, lr, E, s);
+        float m, ssum;
+        float ex[G];
+        if (a.row_stats) {
+            m = a.row_stats[2 * lr];
+            ssum = a.row_stats[2 * lr + 1];
+            const float mL = m * kLog2e;
+#pragma unroll
+            for (int g = 0; g < G; ++g) ex[g] = __builtin_amdgcn_exp2f(fmaf(x[g], kLog2e, -mL));
+        } else {
+            float lmax = x[0];
+#pragma unroll
+            for (int g = 1; g < G; ++g) lmax = fmaxf(lmax, x[g]);
+            m = seg_max<S>(lmax);
+            const float mL = m * kLog2e;
+            ssum = 0.f;
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                ex[g] = __builtin_amdgcn_exp2f(fmaf(x[g], kLog2e, -mL));
+                ssum += ex[g];
+            }
+            ssum = seg_sum<S>(ssum);
+        }
+        const float inv = __builtin_amdgcn_rcpf(ssum);
+        float dot = 0.f;
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            ex[g] *= inv;  // p
+            dot = fmaf(fcol[g], ex[g], dot);
+        }
+        dot = seg_sum<S>(dot);
+        if (valid) {
+            float* dst = a.dlogits + row * E;
+            if constexpr (VEC == 4) {
+#pragma unroll
+                for (int j = 0; j < G / 4; ++j) {
+                    const int c0 = 4 * (j * S + s);
+                    if (!PAD || c0 < E) {
+                        f32x4 v;
+                        v[0] = c * ex[4 * j + 0] * (fcol[4 * j + 0] - dot);
+                        v[1] = c * ex[4 * j + 1] * (fcol[4 * j + 1] - dot);
+                        v[2] = c * ex[4 * j + 2] * (fcol[4 * j + 2] - dot);
+                        v[3] = c * ex[4 * j + 3] * (fcol[4 * j + 3] - dot);
+                        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst + c0));
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const int col = g * S + s;
+                    if (!PAD || col < E) __builtin_nontemporal_store(c * ex[g] * (fcol[g] - dot), dst + col);
+                }
+            }
+        }
+    }
+}
+
+template <int S, int G, int VEC, bool PAD, int NW>
+hipError_t launch_rows_nw(const RowCfg& c, const RowsArgs& a, hipStream_t st) {
+    const size_t lds = rows_lds_bytes(c, a.E, a.k);
+    auto kern = route_rows_kernel<S, G, VEC, PAD, NW>;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(c.B), dim3(NW * 64), lds, st, a);
+    return hipGetLastError();
+}
+
+template <int S, int G, int VEC, bool PAD>
+hipError_t launch_rows(const RowCfg& c, const RowsArgs& a, hipStream_t st) {
+    if (c.NW == 16) return launch_rows_nw<S, G, VEC, PAD, 16>(c, a, st);
+    if (c.NW == 12) return launch_rows_nw<S, G, VEC, PAD, 12>(c, a, st);
+    return hipErrorInvalidValue;
+}
+
+template <int S, int G, int VEC, bool PAD>
+hipError_t launch_backward(const RowCfg& c, const BackArgs& a, hipStream_t st) {
+    if (c.NW == 16)
+        hipLaunchKernelGGL((route_backward_kernel<S, G, VEC, PAD, 16>), dim3(c.B), dim3(16 * 64), 0, st, a);
+    else
+        hipLaunchKernelGGL((route_backward_kernel<S, G, VEC, PAD, 12>), dim3(c.B), dim3(12 * 64), 0, st, a);
+    return hipGetLastError();
+}
+
+// Dispatch over (G, VEC, PAD) for one S.
+template <int S, typename ArgsT, template <int, int, bool> class Launch>
+hipError_t dispatch(const RowCfg& c, const ArgsT& a, hipStream_t st) {
+#define MOE_CASE(GG, VV, PP) \
+    if (c.G == GG && c.VEC == VV && c.PAD == PP) return Launch<GG, VV, PP>::run(c, a, st);
+    MOE_CASE(4, 4, 0) MOE_CASE(8, 4, 0) MOE_CASE(16, 4, 0) MOE_CASE(24, 4, 0)
+    MOE_CASE(4, 4, 1) MOE_CASE(8, 4, 1) MOE_CASE(16, 4, 1) MOE_CASE(24, 4, 1)
+    MOE_CASE(1, 1, 1) MOE_CASE(2, 1, 1) MOE_CASE(4, 1, 1) MOE_CASE(8, 1, 1)
+    MOE_CASE(16, 1, 1) MOE_CASE(24, 1, 1)
+#undef MOE_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace rows_impl
+
+#define MOE_INSTANTIATE_SEGMENT(SV)                                                        \
+    namespace {                                                                            \
+    template <int G, int V, bool P>                                                        \
+    struct RowsL {                                                                         \
+        static hipError_t run(const RowCfg& c, const RowsArgs& a, hipStream_t st) {        \
+            return rows_impl::launch_rows<SV, G, V, P>(c, a, st);                          \
+        }                                                                                  \
+    };                                                                                     \
+    template <int G, int V, bool P>                                                        \
+    struct BackL {                                                                         \
+        static hipError_t run(const RowCfg& c, const BackArgs& a, hipStream_t st) {        \
+            return rows_impl::launch_backward<SV, G, V, P>(c, a, st);                      \
+        }                                                                                  \
+    };                                                                                     \
+    }                                                                                      \
+    template <>                                                                            \
+    hipError_t launch_rows_s<SV>(const RowCfg& c, const RowsArgs& a, hipStream_t st) {     \
+        return rows_impl::dispatch<SV, RowsArgs, RowsL>(c, a, st);                         \
+    }                                                                                      \
+    template <>                                                                            \
+    hipError_t launch_backward_s<SV>(const RowCfg& c, const BackArgs& a, hipStream_t st) { \
+        return rows_impl::dispatch<SV, BackArgs, BackL>(c, a, st);                         \
+    }
+
+}  // namespace moe
