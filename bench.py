@@ -86,6 +86,36 @@ def alg_bytes(w, T):
     return {"rows": rows, "gate": gate, "scatter": scatter, "backward": bwd, "forward": forward}
 
 
+def kernel_source_hash():
+    """Hash of the HIP sources, to tell whether stored counters still apply."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "load_balancing_statistics_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, kernel_prefix):
+    """HBM bytes per launch of a kernel from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary (already scaled by the copy-kernel calibration), or None
+    when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"hbm_bytes_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        lines = fh.read().splitlines()
+    h = [l.split(":")[-1].strip() for l in lines if l.startswith("# kernel sources sha256")]
+    if not h or h[0] != kernel_source_hash():
+        return None
+    for l in lines:
+        if l.startswith(kernel_prefix):
+            parts = l.split()
+            return int(round((float(parts[-2]) + float(parts[-1])) * 1e6))
+    return None
+
+
 def cpu_baseline(w, inp, budget_s):
     import numpy as np
     import oracle
@@ -230,6 +260,7 @@ def main():
         dom_name, dom_bytes, dom_ms = "route_backward_kernel", ab["backward"], bwd_ms
     else:
         dom_name, dom_bytes, dom_ms = "route_rows_kernel", ab["rows"], rows_ms
+    traffic = measured_traffic(w.name, dom_name) if w.d == 0 else None
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     step_bytes = ab["forward"] + ab["backward"]
 
@@ -255,7 +286,7 @@ def main():
                    "renorm": w.renorm, "backward": w.backward},
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": None, "alg_bytes_per_launch": dom_bytes,
+                     "traffic": traffic, "alg_bytes_per_launch": dom_bytes,
                      "launch_ms": round(dom_ms, 5)},
         "cpu_baseline": cpu,
         "detail": {"step_alg_bytes": step_bytes,
