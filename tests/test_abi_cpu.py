@@ -1,0 +1,138 @@
+"""C-ABI checks that need no GPU: exported symbols, struct layout, host-side
+validation and capacity arithmetic.  No call here reaches a HIP launch."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_route.h")
+
+
+@pytest.fixture(scope="module")
+def lbs():
+    import load_balancing_statistics_amd as m
+    from load_balancing_statistics_amd import _binding
+    if not os.path.exists(_binding.LIB_PATH):
+        from load_balancing_statistics_amd import build
+        build.build()
+    m.load()
+    return m
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_route\w*)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported(lbs):
+    lib = lbs.load()
+    names = declared_functions()
+    assert set(names) == {"moe_route", "moe_route_backward", "moe_route_capacity",
+                          "moe_route_strerror", "moe_route_workspace_size"}
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", lbs._binding.LIB_PATH],
+                         capture_output=True, text=True).stdout
+    for n in names:
+        assert re.search(rf"\bT {n}$", out, re.M), f"{n} not exported as a text symbol"
+
+
+def test_struct_layout_matches_header(lbs, tmp_path):
+    """Offsets and sizes of the C structs, printed by a gcc-compiled probe,
+    equal the ctypes mirrors of the binding."""
+    from load_balancing_statistics_amd._binding import moe_route_out, moe_route_params
+    fields_p = [f[0] for f in moe_route_params._fields_]
+    fields_o = [f[0] for f in moe_route_out._fields_]
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "moe_route.h"',
+             'int main(void) {',
+             'printf("P %zu\\n", sizeof(moe_route_params));',
+             'printf("O %zu\\n", sizeof(moe_route_out));']
+    for f in fields_p:
+        lines.append(f'printf("p.{f} %zu\\n", offsetof(moe_route_params, {f}));')
+    for f in fields_o:
+        lines.append(f'printf("o.{f} %zu\\n", offsetof(moe_route_out, {f}));')
+    lines += ['return 0; }']
+    c = tmp_path / "probe.c"
+    c.write_text("\n".join(lines))
+    exe = tmp_path / "probe"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(c), "-o", str(exe)], check=True)
+    got = dict(l.split() for l in subprocess.run([str(exe)], capture_output=True,
+                                                 text=True).stdout.splitlines())
+    assert int(got["P"]) == ctypes.sizeof(moe_route_params)
+    assert int(got["O"]) == ctypes.sizeof(moe_route_out)
+    for f in fields_p:
+        assert int(got[f"p.{f}"]) == getattr(moe_route_params, f).offset, f
+    for f in fields_o:
+        assert int(got[f"o.{f}"]) == getattr(moe_route_out, f).offset, f
+
+
+def test_capacity_and_workspace(lbs):
+    p = lbs.make_params(1024, 8, 1, capacity_factor=1.25)
+    assert lbs.moe_route_capacity(p) == 160
+    assert lbs.moe_route_capacity(lbs.make_params(131072, 256, 8, capacity_factor=1.25)) == 5120
+    assert lbs.moe_route_capacity(lbs.make_params(262144, 384, 6, n_micro=16)) == 256
+    assert lbs.moe_route_capacity(lbs.make_params(100, 8, 2, capacity_factor=0.0)) == -1
+    assert lbs.moe_route_capacity(lbs.make_params(100, 8, 2, capacity=7)) == 7
+    for T, E, k, m, d in [(1, 1, 1, 1, 0), (4096, 8, 1, 1, 0), (131072, 256, 8, 1, 0),
+                          (262144, 384, 6, 16, 0), (16384, 8, 2, 1, 4096), (513, 1024, 32, 1, 0)]:
+        n = lbs.moe_route_workspace_size(lbs.make_params(T, E, k, n_micro=m, d=d))
+        assert 0 < n < 64 * 1024 * 1024
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=0, E=8, k=1), -1), (dict(T=16, E=8, k=0), -1), (dict(T=16, E=8, k=9), -1),
+    (dict(T=15, E=8, k=1, n_micro=2), -1), (dict(T=16, E=2048, k=2), -2),
+    (dict(T=16, E=64, k=33), -2), (dict(T=16, E=8, k=1, d=12), -2),
+    (dict(T=16, E=100, k=2, d=64), -2), (dict(T=16, E=8, k=1, capacity=-5), -1),
+])
+def test_invalid_shapes_rejected(lbs, kw, code):
+    p = lbs.make_params(**kw)
+    with pytest.raises(lbs.MoeRouteError) as ei:
+        lbs.moe_route_workspace_size(p)
+    assert ei.value.code == code
+    assert lbs.moe_route_strerror(code)
+
+
+def test_moe_route_validates_before_launching(lbs):
+    """Missing or misaligned pointers and a short workspace are reported
+    without any device work (there is no GPU here)."""
+    lib = lbs.load()
+    B = lbs._binding
+    p = lbs.make_params(64, 8, 2, save_row_stats=True)
+    fake = 0x10000  # never dereferenced: validation fails first
+    full = {n: fake for n in B._OUT_FIELDS}
+    full["logits"] = None
+
+    def call(out_fields, logits=fake, ws=fake, ws_bytes=1 << 20, params=p):
+        o = B.moe_route_out(*[out_fields.get(n) for n in B._OUT_FIELDS])
+        return lib.moe_route(ctypes.byref(params), logits, None, None, ctypes.byref(o),
+                             ws, ws_bytes, None)
+
+    for missing in ["topk_idx", "topk_w", "counts", "offsets", "perm", "dropped", "aux_loss",
+                    "cv", "max_over_mean", "row_stats"]:
+        f = dict(full)
+        f[missing] = None
+        assert call(f) == B.MOE_ERR_INVALID_ARG, missing
+    assert call(full, logits=None) == B.MOE_ERR_INVALID_ARG
+    assert call(full, logits=fake + 2) == B.MOE_ERR_INVALID_ARG  # misaligned
+    assert call(full, ws=None) == B.MOE_ERR_WORKSPACE
+    assert call(full, ws_bytes=16) == B.MOE_ERR_WORKSPACE
+    assert call(full, ws=fake + 8) == B.MOE_ERR_WORKSPACE       # not 256-byte aligned
+    pi = lbs.make_params(64, 8, 2, inv_perm=True)
+    f = dict(full)
+    f["inv_perm"] = None
+    assert call(f, params=pi) == B.MOE_ERR_INVALID_ARG
+    pg = lbs.make_params(64, 8, 2, d=64)
+    assert call(full, params=pg) == B.MOE_ERR_INVALID_ARG        # gate path without X/Wg
+    assert lib.moe_route(None, None, None, None, None, None, 0, None) == B.MOE_ERR_INVALID_ARG
+    # backward
+    assert lib.moe_route_backward(ctypes.byref(p), None, None, fake, None, fake, None) \
+        == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_backward(ctypes.byref(p), fake, None, None, None, fake, None) \
+        == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_backward(ctypes.byref(p), fake + 1, None, fake, None, fake, None) \
+        == B.MOE_ERR_INVALID_ARG
