@@ -45,6 +45,11 @@ def build(jobs=None, verbose=False):
     os.makedirs(OBJ_DIR, exist_ok=True)
     os.makedirs(LIB_DIR, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    # objects of sources that no longer exist must not linger
+    keep = {os.path.basename(p) + ".o" for p in srcs}
+    for o in glob.glob(os.path.join(OBJ_DIR, "*.o")):
+        if os.path.basename(o) not in keep:
+            os.remove(o)
     jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 4)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(_compile, srcs))

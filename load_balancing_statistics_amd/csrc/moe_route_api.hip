@@ -1,6 +1,6 @@
 // moe_route_api.hip -- the C ABI declared in include/moe_route.h: argument
 // validation on the host, workspace sizing, and the launch sequence
-//   [gate transpose + gate GEMM] -> row pass -> block scan -> statistics
+//   [gate transpose + gate GEMM] -> row pass -> block scan + statistics
 //   -> dispatch scatter
 // for the forward, and the single streaming pass of the backward.
 #include <climits>
@@ -29,6 +29,7 @@ int check_shape(const moe_route_params* p) {
     if (p->d > 0 && !moe::gate_supported(p->T, p->d, p->E)) return MOE_ERR_UNSUPPORTED;
     const RowCfg c = moe::choose_rows(p->T, p->E, p->k, p->n_micro);
     if (c.G < 0 || moe::rows_lds_bytes(c, p->E, p->k) > kMaxLds) return MOE_ERR_UNSUPPORTED;
+    if (moe::scatter_lds_bytes(p->E, p->k) > kMaxLds) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -143,6 +144,7 @@ int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
     ra.qcap = moe::rows_queue_cap(c);
     ra.topk_idx = out->topk_idx; ra.topk_w = out->topk_w; ra.row_stats = out->row_stats;
     ra.cnt_part = ws.cnt_part; ra.P_part = ws.P_part; ra.flag_part = ws.flag_part;
+    ra.arrive = ws.arrive; ra.n_micro = p->n_micro;
     const bool timed = out->row_pass_events[0] && out->row_pass_events[1];
     if (timed && hipEventRecord(static_cast<hipEvent_t>(out->row_pass_events[0]), st) != hipSuccess)
         return MOE_ERR_HIP;
@@ -152,24 +154,20 @@ int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
 
     moe::ScanArgs sa{};
     sa.cnt_part = ws.cnt_part; sa.P_part = ws.P_part; sa.flag_part = ws.flag_part;
-    sa.E = p->E; sa.bpm = c.bpm; sa.n_micro = p->n_micro; sa.B = c.B; sa.nsplit = c.nsplit;
+    sa.E = p->E; sa.k = p->k; sa.Tm = Tm; sa.bpm = c.bpm; sa.n_micro = p->n_micro; sa.B = c.B;
+    sa.nsplit = c.nsplit; sa.capacity = int(capacity_of(p)); sa.alpha = p->alpha;
     sa.colprefix = ws.colprefix; sa.split_tot = ws.split_tot; sa.split_P = ws.split_P;
-    sa.status = out->status;
+    sa.arrive = ws.arrive; sa.status = out->status;
+    sa.counts = out->counts; sa.offsets = out->offsets; sa.f = out->f; sa.P = out->P;
+    sa.aux = out->aux_loss; sa.cv = out->cv; sa.max_over_mean = out->max_over_mean;
+    sa.extra = out->extra_stats;
     if (moe::launch_route_scan(c, sa, st) != hipSuccess) return MOE_ERR_HIP;
-
-    moe::FinalArgs fa{};
-    fa.split_tot = ws.split_tot; fa.split_P = ws.split_P;
-    fa.E = p->E; fa.k = p->k; fa.Tm = Tm; fa.nsplit = c.nsplit;
-    fa.capacity = int(capacity_of(p)); fa.alpha = p->alpha;
-    fa.counts = out->counts; fa.offsets = out->offsets; fa.f = out->f; fa.P = out->P;
-    fa.aux = out->aux_loss; fa.cv = out->cv; fa.max_over_mean = out->max_over_mean;
-    fa.extra = out->extra_stats;
-    if (moe::launch_route_finalize(c, fa, p->n_micro, st) != hipSuccess) return MOE_ERR_HIP;
 
     moe::ScatterArgs ca{};
     ca.topk_idx = out->topk_idx; ca.colprefix = ws.colprefix; ca.split_tot = ws.split_tot;
-    ca.T = p->T; ca.E = p->E; ca.k = p->k; ca.Tm = Tm; ca.R = c.R; ca.bpm = c.bpm;
-    ca.nsplit = c.nsplit;
+    ca.offsets = out->offsets;
+    ca.T = p->T; ca.E = p->E; ca.k = p->k; ca.Tm = Tm; ca.bpm = c.bpm; ca.nsplit = c.nsplit;
+    ca.rows_per_wave = moe::scatter_rows_per_wave(p->E, p->k);
     ca.capacity = int(capacity_of(p));
     ca.perm = out->perm;
     ca.inv_perm = (p->flags & MOE_WRITE_INV_PERM) ? out->inv_perm : nullptr;

@@ -133,6 +133,7 @@ struct Workspace {
     int32_t* colprefix;   // [B,E]        exclusive prefix over the blocks of a split
     int32_t* split_tot;   // [m,nsplit,E] counts per split
     double*  split_P;     // [m,nsplit,E] probability sums per split
+    int32_t* arrive;      // [m]          scan blocks finished per microbatch
     uint16_t* Wt;         // [E,d]        transposed gate weights (gate path only)
     size_t   bytes;
 };
@@ -152,6 +153,7 @@ inline Workspace carve_workspace(void* base, const RowCfg& c, int E, int m, size
     size_t o_pre = take(B * E * 4);
     size_t o_tot = take(size_t(m) * ns * E * 4);
     size_t o_ps = take(size_t(m) * ns * E * 8);
+    size_t o_arr = take(size_t(m) * 4);
     size_t o_wt = take(gate_bytes);
     w.bytes = off;
     char* b = static_cast<char*>(base);
@@ -162,6 +164,7 @@ inline Workspace carve_workspace(void* base, const RowCfg& c, int E, int m, size
         w.colprefix = reinterpret_cast<int32_t*>(b + o_pre);
         w.split_tot = reinterpret_cast<int32_t*>(b + o_tot);
         w.split_P = reinterpret_cast<double*>(b + o_ps);
+        w.arrive = reinterpret_cast<int32_t*>(b + o_arr);
         w.Wt = gate_bytes ? reinterpret_cast<uint16_t*>(b + o_wt) : nullptr;
     }
     return w;
@@ -179,37 +182,23 @@ struct RowsArgs {
     int32_t* cnt_part;
     float* P_part;
     int32_t* flag_part;
+    int32_t* arrive;  // [n_micro] zeroed by block 0 for the scan that follows
+    int n_micro;
 };
 
 struct ScanArgs {
     const int32_t* cnt_part;
     const float* P_part;
     const int32_t* flag_part;
-    int E, bpm, n_micro, B, nsplit;
+    int E, k, Tm, bpm, n_micro, B, nsplit;
+    int capacity;  // < 0: unlimited
+    float alpha;
     int32_t* colprefix;
     int32_t* split_tot;
     double* split_P;
+    int32_t* arrive;
     int32_t* status;
-};
-
-struct ScatterArgs {
-    const int32_t* topk_idx;
-    const int32_t* colprefix;
-    const int32_t* split_tot;
-    int T, E, k, Tm, R, bpm, nsplit;
-    int capacity;  // < 0: unlimited
-    int32_t* perm;
-    int32_t* inv_perm;
-    uint8_t* dropped;
-    int32_t* status;
-};
-
-struct FinalArgs {
-    const int32_t* split_tot;
-    const double* split_P;
-    int E, k, Tm, nsplit;
-    int capacity;  // < 0: unlimited
-    float alpha;
+    // per-microbatch statistics, written by the last scan block of each
     int32_t* counts;
     int32_t* offsets;
     float* f;
@@ -218,6 +207,20 @@ struct FinalArgs {
     float* cv;
     float* max_over_mean;
     float* extra;
+};
+
+struct ScatterArgs {
+    const int32_t* topk_idx;
+    const int32_t* colprefix;
+    const int32_t* split_tot;
+    const int32_t* offsets;
+    int T, E, k, Tm, bpm, nsplit;
+    int rows_per_wave;  // rows a wave ranks per window (<= 64, one mask bit each)
+    int capacity;  // < 0: unlimited
+    int32_t* perm;
+    int32_t* inv_perm;
+    uint8_t* dropped;
+    int32_t* status;
 };
 
 struct BackArgs {
@@ -251,7 +254,8 @@ MOE_DECLARE_SEGMENT(16) MOE_DECLARE_SEGMENT(32) MOE_DECLARE_SEGMENT(64)
 #undef MOE_DECLARE_SEGMENT
 hipError_t launch_route_scan(const RowCfg& c, const ScanArgs& a, hipStream_t st);
 hipError_t launch_route_scatter(const RowCfg& c, const ScatterArgs& a, hipStream_t st);
-hipError_t launch_route_finalize(const RowCfg& c, const FinalArgs& a, int n_micro, hipStream_t st);
+int scatter_rows_per_wave(int E, int k);
+size_t scatter_lds_bytes(int E, int k);
 hipError_t launch_route_backward(const RowCfg& c, const BackArgs& a, hipStream_t st);
 hipError_t launch_gate_gemm(const GateArgs& a, uint16_t* wt, hipStream_t st);
 bool gate_supported(int T, int d, int E);
@@ -443,6 +447,56 @@ MOE_DEV uint64_t seg_max_u64(uint64_t v) {
 MOE_DEV double shfl_xor_f64(double v, int m) {
     uint64_t u = __double_as_longlong(v);
     return __longlong_as_double((long long)shfl_xor_u64(u, m));
+}
+
+// Whole-wave reductions without LDS traffic: butterflies inside each 16-lane
+// row through DPP (every lane of a row ends with the row's value), then the
+// four rows combined in row order from readlanes.  Deterministic; the result
+// is wave-uniform.
+template <int D>
+MOE_DEV double xstep_f64(double v) {
+    const int lo = xstepi<D>(__double2loint(v));
+    const int hi = xstepi<D>(__double2hiint(v));
+    return __hiloint2double(hi, lo);
+}
+MOE_DEV double readlane_f64(double v, int l) {
+    const int lo = __builtin_amdgcn_readlane(__double2loint(v), l);
+    const int hi = __builtin_amdgcn_readlane(__double2hiint(v), l);
+    return __hiloint2double(hi, lo);
+}
+MOE_DEV double wave_sum_f64(double v) {
+    v += xstep_f64<1>(v);
+    v += xstep_f64<2>(v);
+    v += xstep_f64<4>(v);
+    v += xstep_f64<8>(v);
+    return ((readlane_f64(v, 0) + readlane_f64(v, 16)) + readlane_f64(v, 32)) + readlane_f64(v, 48);
+}
+MOE_DEV int wave_max_i(int v) {
+    v = max(v, xstepi<1>(v));
+    v = max(v, xstepi<2>(v));
+    v = max(v, xstepi<4>(v));
+    v = max(v, xstepi<8>(v));
+    return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+MOE_DEV int wave_min_i(int v) {
+    v = min(v, xstepi<1>(v));
+    v = min(v, xstepi<2>(v));
+    v = min(v, xstepi<4>(v));
+    v = min(v, xstepi<8>(v));
+    return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+// Inclusive prefix sum over the 64 lanes of a wave.
+MOE_DEV int wave_incl_scan_i(int v) { return seg_incl_scan<64>(v, __lane_id()); }
+
+// Load p[i] when ok, else return dflt -- always from a valid address (index 0
+// stands in), so the load is issued unconditionally and independent loads
+// overlap instead of each waiting inside its own branch.
+template <class T>
+MOE_DEV T load_or(const T* p, long i, bool ok, T dflt) {
+    const T v = p[ok ? i : 0];
+    return ok ? v : dflt;
 }
 
 }  // namespace dev

@@ -343,6 +343,8 @@ route_rows_kernel(const RowsArgs a)
     block_rows(blockIdx.x, a.bpm, a.Tm, row_begin, row_end);
 
     for (int e = tid; e < E; e += NW * 64) hist[e] = 0;
+    if (blockIdx.x == 0)
+        for (int m = tid; m < a.n_micro; m += NW * 64) a.arrive[m] = 0;
     __syncthreads();
 
     float* rowbuf = rowbuf_all + (wave * W + seg) * RS;

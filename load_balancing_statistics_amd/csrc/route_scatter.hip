@@ -8,9 +8,19 @@
 // assignments to expert e start at
 //   offsets[e] + (count of e in the earlier splits) + (count of e in the
 //   earlier blocks of its split).
-// Inside the block each wave takes a contiguous slice; within a 64-assignment
-// chunk the rank among equal experts comes from ballots over the expert-id
-// bits, so the order is exact and deterministic.
+//
+// A token picks an expert at most once (its top-k are distinct), so inside an
+// expert the (t, j) order is the token order.  The block walks its rows in
+// windows; in a window each wave owns a contiguous run of rows, row r of the
+// run being bit r of a 64-bit mask per (wave, expert).  Every slot (r, j)
+// ORs its bit into the mask of its expert; a slot's rank among the wave's
+// assignments to that expert is then the popcount of the mask below its bit,
+// and the wave's count is the whole popcount.  An exclusive scan over the
+// waves and one over the experts place every slot in an LDS copy of the
+// window sorted by expert, which is written to the permutation in that order:
+// the block's assignments to one expert land in consecutive words, so the
+// stores coalesce.  dropped and inv_perm are indexed by the assignment and
+// are stored from the ranking pass.
 #include "route_common.hpp"
 
 namespace moe {
@@ -18,183 +28,238 @@ namespace {
 
 using namespace dev;
 
-constexpr int kScatWaves = 16;
-constexpr int kScatThreads = kScatWaves * 64;
-constexpr int kCachedChunks = 8;  // 64-assignment chunks kept in registers per wave
+constexpr int kScatMaxWaves = 16;
+constexpr int kSplitBatch = 8;
 
-// In-place exclusive scan of n LDS ints v[0..n) into out[0..n] (out[n] = total).
+// Exclusive scan of n LDS ints v[0..n) into out[0..n] (out[n] = total).
 __device__ void block_excl_scan(const int* v, int n, int* out, int* wsum) {
+    const int nthr = blockDim.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int per = (n + kScatThreads - 1) / kScatThreads;
+    const int per = (n + nthr - 1) / nthr;
     const int i0 = min(tid * per, n), i1 = min(i0 + per, n);
+    const bool busy = wave * 64 * per < n;  // wave-uniform: the wave holds entries
     int loc = 0;
     for (int i = i0; i < i1; ++i) loc += v[i];
-    int incl = loc;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        int t = __shfl_up(incl, d);
-        if (lane >= d) incl += t;
+    int incl = 0;
+    if (busy) {
+        incl = wave_incl_scan_i(loc);
+        if (lane == 63) wsum[wave] = incl;
     }
-    if (lane == 63) wsum[wave] = incl;
     __syncthreads();
-    int wbase = 0;
-    for (int w = 0; w < wave; ++w) wbase += wsum[w];
-    int run = wbase + incl - loc;
-    for (int i = i0; i < i1; ++i) {
-        const int t = v[i];
-        out[i] = run;
-        run += t;
+    if (busy) {
+        int run = incl - loc;
+        for (int w = 0; w < wave; ++w) run += wsum[w];
+        for (int i = i0; i < i1; ++i) {
+            const int t = v[i];
+            out[i] = run;
+            run += t;
+        }
+        if (i1 == n && i0 < n) out[n] = run;
     }
-    if (tid == kScatThreads - 1) out[n] = run;
+    if (n == 0 && tid == 0) out[0] = 0;
     __syncthreads();
 }
 
-__global__ void __launch_bounds__(kScatThreads)
+// Logical block of a workgroup: workgroups are dealt to the 8 XCDs in turn,
+// so consecutive logical blocks -- whose runs of each expert are adjacent in
+// the permutation -- are given to workgroups of one XCD, and the partial
+// cache lines they share meet in one L2.
+__device__ __forceinline__ int logical_block() {
+    const int n = gridDim.x, b = blockIdx.x;
+    return (n % 8 == 0) ? (b % 8) * (n / 8) + b / 8 : b;
+}
+
+// Slots (r, j) a lane ranks per window: rows get 64/rows-per-wave lanes, and
+// the host caps rows per wave at 64/next_pow2(ceil(k/KM)), so ceil(k/lanes)
+// never exceeds KM.
+constexpr int KM = 8;
+
+__global__ void __launch_bounds__(kScatMaxWaves * 64)
 route_scatter_kernel(const ScatterArgs a)
 {
-    extern __shared__ __align__(16) int sm[];
-    const int E = a.E;
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int E = a.E, k = a.k;
+    const int NW = int(blockDim.x) >> 6;
     const int E4 = (E + 1 + 3) & ~3;
-    int* offs = sm;             // [E+1]
-    int* tot = sm + E4;         // [E]
-    int* base = tot + E4;       // [E]
-    int* wh = base + E4;        // [kScatWaves][E]
-    __shared__ int wsum[kScatWaves];
+    uint64_t* gm = reinterpret_cast<uint64_t*>(smem);      // [NW][E] row masks
+    int2* rec = reinterpret_cast<int2*>(gm + NW * E);       // [NW][E] {window place, segment place} of the wave's first
+    int2* st = rec + NW * E;                                // [stage] {assignment, segment place}, expert order
+    int* base = reinterpret_cast<int*>(st + NW * a.rows_per_wave * k);  // [E] the block's next place for e
+    int* lim = base + E4;                                   // [E] first dropped place of e
+    int* tot = lim + E4;                                    // [E4] window counts
+    int* lofs = tot + E4;                                   // [E4] window-local expert starts
+    __shared__ int wsum[kScatMaxWaves];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int mb = blockIdx.x / a.bpm, bi = blockIdx.x - (blockIdx.x / a.bpm) * a.bpm;
+    const int b = logical_block();
+    const int mb = b / a.bpm, bi = b - mb * a.bpm;
     const int my_split = bi / (kScanWaves * kScanPerWave);
     long row_begin, row_end;
-    block_rows(blockIdx.x, a.bpm, a.Tm, row_begin, row_end);
-    const long segment = long(mb) * a.Tm * a.k;  // start of the microbatch in perm
-    const long seglen = long(a.Tm) * a.k;
+    block_rows(b, a.bpm, a.Tm, row_begin, row_end);
+    const long segment = long(mb) * a.Tm * k;  // start of the microbatch in perm
+    const long seglen = long(a.Tm) * k;
+    const int WR = NW * a.rows_per_wave;       // rows per window
 
-    // this block's assignments, one contiguous slice per wave
-    const long a0 = row_begin * a.k, a1 = row_end * a.k;
-    long q = (a1 - a0 + kScatWaves - 1) / kScatWaves;
-    q = (q + 63) & ~63L;
-    const long s0 = min(a0 + wave * q, a1), s1 = min(s0 + q, a1);
-
-    // ---- issue every independent global load first
-    int eid[kCachedChunks];
+    // slot layout of a window: rows per wave, lanes per row
+    int ev[KM];
+    long row = 0;
+    int rl = 0, g = 0, lpr = 1;
+    bool active = false;
+    auto load_window = [&](long w0) {
+        const long w1 = min(w0 + long(WR), row_end);
+        const int nrows = int(w1 - w0);
+        const int rpw = (nrows + NW - 1) / NW;
+        int rp = 1;
+        while (rp < rpw) rp <<= 1;
+        lpr = 64 / rp;
+        rl = lane & (rp - 1);
+        g = lane / rp;
+        row = w0 + long(wave) * rpw + rl;
+        active = rl < rpw && row < w1;
 #pragma unroll
-    for (int u = 0; u < kCachedChunks; ++u) {
-        const long i = s0 + long(u) * 64 + lane;
-        eid[u] = (i < s1) ? a.topk_idx[i] : -1;
-    }
-    for (int e = tid; e < E; e += kScatThreads) {
-        tot[e] = 0;
-        base[e] = a.colprefix[long(blockIdx.x) * E + e];
-    }
-    for (int i = tid; i < kScatWaves * E; i += kScatThreads) wh[i] = 0;
-    __syncthreads();
-    // per-split counts: all (split, expert) pairs loaded at once, summed with
-    // integer LDS atomics (order-independent)
-    {
-        const int n = a.nsplit * E;
-        const int32_t* st = a.split_tot + long(mb) * n;
-        for (int i0 = 0; i0 < n; i0 += 4 * kScatThreads) {
-            int v[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int i = i0 + u * kScatThreads + tid;
-                v[u] = (i < n) ? st[i] : 0;
-            }
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int i = i0 + u * kScatThreads + tid;
-                if (i < n) {
-                    const int sp = i / E, e = i - sp * E;
-                    atomicAdd(&tot[e], v[u]);
-                    if (sp < my_split) atomicAdd(&base[e], v[u]);
-                }
-            }
+        for (int u = 0; u < KM; ++u) {
+            const int j = g + u * lpr;
+            ev[u] = load_or(a.topk_idx, row * k + j, active && j < k, -1);
         }
+    };
+    load_window(row_begin);
+    for (int e = tid; e < E; e += blockDim.x) {
+        // counts of the earlier splits: the first kSplitBatch loaded with the
+        // offset and the prefix, in one round
+        const long sb = long(mb) * a.nsplit * E + e;
+        int sv[kSplitBatch];
+#pragma unroll
+        for (int v = 0; v < kSplitBatch; ++v) sv[v] = load_or(a.split_tot, sb + long(v) * E, v < my_split, 0);
+        const int o = a.offsets[long(mb) * (E + 1) + e];
+        int bs = o + a.colprefix[long(b) * E + e];
+#pragma unroll
+        for (int v = 0; v < kSplitBatch; ++v) bs += sv[v];
+        for (int sp = kSplitBatch; sp < my_split; ++sp) bs += a.split_tot[sb + long(sp) * E];
+        const long l = a.capacity >= 0 ? long(o) + a.capacity : long(INT32_MAX);
+        base[e] = bs;
+        lim[e] = int(l < INT32_MAX ? l : INT32_MAX);
     }
-    __syncthreads();
 
-    block_excl_scan(tot, E, offs, wsum);
-    for (int e = tid; e < E; e += kScatThreads) base[e] += offs[e];
-
-    // ---- per-wave histogram of the slice, then per-wave bases
-    int* mywh = wh + wave * E;
+    uint64_t* mym = gm + wave * E;
+    const int2* myrec = rec + wave * E;
     int internal = 0;
+    for (long w0 = row_begin; w0 < row_end; w0 += WR) {
+        if (w0 != row_begin) load_window(w0);
+        // this wave's masks (wave-private until the barrier)
+        for (int e = lane; e < E; e += 64) mym[e] = 0;
+        const uint64_t bit = 1ull << rl;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int u = 0; u < kCachedChunks; ++u) {
-        const int e = eid[u];
-        if (e >= 0 && e < E) atomicAdd(&mywh[e], 1);
-    }
-    for (long c = s0 + long(kCachedChunks) * 64; c < s1; c += 64) {
-        const long i = c + lane;
-        if (i < s1) {
-            const int e = a.topk_idx[i];
-            if (e >= 0 && e < E) atomicAdd(&mywh[e], 1);
+        for (int u = 0; u < KM; ++u) {
+            const int e = ev[u];
+            if (e >= 0 && e < E) atomicOr(reinterpret_cast<unsigned long long*>(&mym[e]), bit);
+            else if (active && g + u * lpr < k) internal = 1;
         }
-    }
-    __syncthreads();
-    for (int e = tid; e < E; e += kScatThreads) {
-        int run = base[e];
-        for (int w = 0; w < kScatWaves; ++w) {
-            const int t = wh[w * E + e];
-            wh[w * E + e] = run;
-            run += t;
+        __syncthreads();
+        // window count of every expert
+        for (int e = tid; e < E; e += blockDim.x) {
+            int c[kScatMaxWaves];
+#pragma unroll
+            for (int w = 0; w < kScatMaxWaves; ++w) c[w] = (w < NW) ? __popcll(gm[w * E + e]) : 0;
+            int t = 0;
+#pragma unroll
+            for (int w = 0; w < kScatMaxWaves; ++w) t += c[w];
+            tot[e] = t;
         }
-    }
-    __syncthreads();
+        __syncthreads();
+        block_excl_scan(tot, E, lofs, wsum);
+        const int nvalid = lofs[E];
+        // per (wave, expert): where the wave's first assignment to e goes,
+        // inside the window and inside the segment
+        for (int e = tid; e < E; e += blockDim.x) {
+            int c[kScatMaxWaves];
+#pragma unroll
+            for (int w = 0; w < kScatMaxWaves; ++w) c[w] = (w < NW) ? __popcll(gm[w * E + e]) : 0;
+            int lp = lofs[e], sp = base[e];
+#pragma unroll
+            for (int w = 0; w < kScatMaxWaves; ++w) {
+                if (w < NW) rec[w * E + e] = make_int2(lp, sp);
+                lp += c[w];
+                sp += c[w];
+            }
+        }
+        __syncthreads();
 
-    // ---- stable ranks inside 64-assignment chunks, in order
-    int nbits = 0;
-    while ((1 << nbits) < E) ++nbits;
-    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    int u = 0;
-    for (long c = s0; c < s1; c += 64, ++u) {
-        const long i = c + lane;
-        bool valid = i < s1;
-        int e;
-        if (u < kCachedChunks) {
-            e = eid[0];
+        // every slot: rank among the wave's assignments to its expert, places
+        const uint64_t below = bit - 1;
+        const long ibase = row * k;
 #pragma unroll
-            for (int v = 1; v < kCachedChunks; ++v) e = (u == v) ? eid[v] : e;
-        } else {
-            e = valid ? a.topk_idx[i] : 0;
-        }
-        if (valid && (e < 0 || e >= E)) {
-            internal = 1;
-            valid = false;
-        }
-        if (!valid) e = 0;
-        uint64_t peers = __ballot(valid);
-        for (int bt = 0; bt < nbits; ++bt) {
-            const bool bit = (e >> bt) & 1;
-            const uint64_t bal = __ballot(bit);
-            peers &= bit ? bal : ~bal;
-        }
-        const int before = __popcll(peers & lt);
-        const int cnt = __popcll(peers);
-        const int basepos = mywh[e];
-        const bool leader = valid && (63 - __clzll(peers)) == lane;
-        if (leader) mywh[e] = basepos + cnt;
-        if (valid) {
-            const int pos = basepos + before;
-            if (pos < 0 || pos >= seglen) {
-                internal = 1;
-            } else {
-                const int r = pos - offs[e];
-                a.dropped[i] = (a.capacity >= 0 && r >= a.capacity) ? 1 : 0;
-                a.perm[segment + pos] = int32_t(i);
+        for (int u = 0; u < KM; ++u) {
+            const int e = ev[u];
+            if (e < 0 || e >= E) continue;
+            const int j = g + u * lpr;
+            const int rank = __popcll(mym[e] & below);
+            const int2 r = myrec[e];
+            const int lp = r.x + rank;
+            const long pos = long(r.y) + rank;
+            const long i = ibase + j;
+            const bool in_seg = pos >= 0 && pos < seglen;
+            if (lp < 0 || lp >= nvalid || !in_seg) internal = 1;
+            if (lp >= 0 && lp < nvalid) st[lp] = make_int2(int(i), in_seg ? int(pos) : -1);
+            if (in_seg) {
+                a.dropped[i] = (pos >= lim[e]) ? 1 : 0;
                 if (a.inv_perm) a.inv_perm[i] = int32_t(segment + pos);
             }
         }
+        __syncthreads();
+        // the window in expert order: runs of consecutive places
+        for (int p = tid; p < nvalid; p += blockDim.x) {
+            const int2 v = st[p];
+            if (v.y >= 0 && v.y < seglen) a.perm[segment + v.y] = v.x;
+        }
+        for (int e = tid; e < E; e += blockDim.x) base[e] += tot[e];
+        __syncthreads();
     }
     if (internal && a.status) atomicOr(a.status, MOE_STATUS_INTERNAL);
 }
 
+int scatter_waves(int E) { return E <= 512 ? 16 : 8; }
+
+int rows_cap_for_k(int k) {
+    int lanes = 1;
+    while (lanes * KM < k) lanes <<= 1;
+    return 64 / lanes;
+}
+
+size_t lds_for(int E, int NW, int rpw, int k) {
+    const size_t E4 = size_t((E + 1 + 3) & ~3);
+    const size_t stage = size_t(NW) * rpw * k;
+    return size_t(NW) * E * 16 + stage * 8 + 4 * E4 * 4;
+}
+
 }  // namespace
 
+// Rows per wave and window: 64 (one mask bit per row), halved until the
+// block's LDS fits.
+int scatter_rows_per_wave(int E, int k) {
+    const int NW = scatter_waves(E);
+    int rpw = rows_cap_for_k(k);
+    while (rpw > 1 && lds_for(E, NW, rpw, k) > 160 * 1024) rpw >>= 1;
+    return rpw;
+}
+
+size_t scatter_lds_bytes(int E, int k) {
+    return lds_for(E, scatter_waves(E), scatter_rows_per_wave(E, k), k);
+}
+
 hipError_t launch_route_scatter(const RowCfg& c, const ScatterArgs& a, hipStream_t st) {
-    const size_t E4 = size_t((a.E + 1 + 3) & ~3);
-    const size_t lds = (3 * E4 + size_t(kScatWaves) * a.E) * 4;
-    hipLaunchKernelGGL(route_scatter_kernel, dim3(c.B), dim3(kScatThreads), lds, st, a);
+    const int NW = scatter_waves(a.E);
+    const size_t lds = lds_for(a.E, NW, a.rows_per_wave, a.k);
+    if (a.k > MOE_ROUTE_MAX_K || a.E > MOE_ROUTE_MAX_E || a.rows_per_wave < 1 ||
+        a.rows_per_wave > rows_cap_for_k(a.k))
+        return hipErrorInvalidValue;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(route_scatter_kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(route_scatter_kernel, dim3(c.B), dim3(NW * 64), lds, st, a);
     return hipGetLastError();
 }
 
