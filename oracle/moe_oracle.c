@@ -19,6 +19,9 @@
  *        zero-count experts), 4.2 (distribution ratio, entropy).
  *   [p3] cnvsn.com/news/335486, survey of load balancing for large models:
  *        sections 3.1 and 5.1 (coefficient of variation, balance degree).
+ *   [p1] section 4.3 also gives the loss-free variant: a per-expert scalar
+ *        bias on the router logits, moved down for overloaded experts and up
+ *        for idle ones (selection bias and its update, below).
  * Readings where the pages are silent are stated at each function.
  */
 #include <math.h>
@@ -88,10 +91,11 @@ static void softmax_stats(const double *row, long long E, double *m_out, double 
 
 /*
  * Top-k selection for one row: the first k experts in the order
- * (logit descending, expert index ascending).  Comparison is numeric, so
- * -0.0 and +0.0 are equal and the lower index wins.  Written as k passes of
- * "take the best expert not taken yet"; a strict '>' keeps the lowest index
- * among equal logits.
+ * (selection value descending, expert index ascending), where the selection
+ * value is the logit itself or, with a selection bias, the biased logit.
+ * Comparison is numeric, so -0.0 and +0.0 are equal and the lower index
+ * wins.  Written as k passes of "take the best expert not taken yet"; a
+ * strict '>' keeps the lowest index among equal values.
  */
 static void topk_row(const double *row, long long E, long long k, int32_t *idx, char *taken)
 {
@@ -113,6 +117,12 @@ static void topk_row(const double *row, long long E, long long k, int32_t *idx, 
  * Forward routing of T tokens split into n_micro equal microbatches of
  * Tm = T / n_micro tokens; every microbatch is routed on its own.
  *
+ * select_bias [E] (may be NULL): [p1] 4.3 adds a per-expert scalar b_i to
+ * the router logits to steer the choice.  Reading: the bias enters the
+ * selection only -- the gate weights, the probabilities behind P_i and the
+ * aux loss keep the unbiased softmax -- and the biased value is the fp32 sum
+ * l + b_i (the precision the logits and the bias are given in).
+ *
  * Outputs (all caller-allocated; pointers marked "may be NULL" are skipped):
  *   topk_idx [T*k], topk_w [T*k]          selection and gate weights
  *   row_max, row_sum [T]      (may be NULL) softmax statistics
@@ -130,7 +140,7 @@ static void topk_row(const double *row, long long E, long long k, int32_t *idx, 
  */
 int oracle_route(const double *logits, long long T, long long E, long long k,
                  long long n_micro, long long capacity, double alpha, int renorm,
-                 int32_t *topk_idx, double *topk_w, double *row_max, double *row_sum,
+                 const float *select_bias, int32_t *topk_idx, double *topk_w, double *row_max, double *row_sum,
                  int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm,
                  uint8_t *dropped, double *f, double *P, double *aux, double *cv,
                  double *max_over_mean, double *extra)
@@ -141,8 +151,9 @@ int oracle_route(const double *logits, long long T, long long E, long long k,
     char *taken = (char *)malloc((size_t)E);
     double *psum = (double *)malloc(sizeof(double) * (size_t)E);
     long long *cursor = (long long *)malloc(sizeof(long long) * (size_t)E);
-    if (!taken || !psum || !cursor) {
-        free(taken); free(psum); free(cursor);
+    double *selrow = (double *)malloc(sizeof(double) * (size_t)E);
+    if (!taken || !psum || !cursor || !selrow) {
+        free(taken); free(psum); free(cursor); free(selrow);
         return -1;
     }
 
@@ -169,7 +180,15 @@ int oracle_route(const double *logits, long long T, long long E, long long k,
                 psum[e] += exp(row[e] - m) / s;
 
             int32_t *idx = topk_idx + t * k;
-            topk_row(row, E, k, idx, taken);
+            if (select_bias) {
+                for (long long e = 0; e < E; ++e) {
+                    float biased = (float)row[e] + select_bias[e];
+                    selrow[e] = (double)biased;
+                }
+                topk_row(selrow, E, k, idx, taken);
+            } else {
+                topk_row(row, E, k, idx, taken);
+            }
             double picked = 0.0;
             for (long long j = 0; j < k; ++j)
                 picked += exp(row[idx[j]] - m) / s;
@@ -245,7 +264,33 @@ int oracle_route(const double *logits, long long T, long long E, long long k,
     free(taken);
     free(psum);
     free(cursor);
+    free(selrow);
     return 0;
+}
+
+/*
+ * Update of the selection bias after a forward pass.  [p1] 4.3: an
+ * overloaded expert's b_i is pushed down, an idle one's up, and no loss term
+ * is involved.  The page gives no step form; reading: a fixed step gamma
+ * against the sign of the expert's load error, in fp32,
+ *   load_e = sum over microbatches of counts[mb][e]  (pre-capacity),
+ *   b_e <- b_e - gamma  if load_e > T*k/E,
+ *   b_e <- b_e + gamma  if load_e < T*k/E,  unchanged if equal.
+ * The comparison is done exactly in integers (load_e * E against T * k).
+ */
+void oracle_bias_update(const int32_t *counts, long long n_micro, long long E,
+                        long long T, long long k, float gamma, float *bias)
+{
+    for (long long e = 0; e < E; ++e) {
+        long long load = 0;
+        for (long long mb = 0; mb < n_micro; ++mb)
+            load += counts[mb * E + e];
+        long long lhs = load * E, rhs = T * k;
+        if (lhs > rhs)
+            bias[e] = bias[e] - gamma;
+        else if (lhs < rhs)
+            bias[e] = bias[e] + gamma;
+    }
 }
 
 /*

@@ -27,10 +27,12 @@ def load_library(path=None):
     lib.oracle_capacity.restype = ll
     lib.oracle_gate_logits.argtypes = [vp, vp, ll, ll, ll, vp]
     lib.oracle_gate_logits.restype = None
-    lib.oracle_route.argtypes = [vp, ll, ll, ll, ll, ll, d, i] + [vp] * 15
+    lib.oracle_route.argtypes = [vp, ll, ll, ll, ll, ll, d, i] + [vp] * 16
     lib.oracle_route.restype = i
     lib.oracle_backward.argtypes = [vp, ll, ll, ll, ll, d, vp, vp, vp]
     lib.oracle_backward.restype = None
+    lib.oracle_bias_update.argtypes = [vp, ll, ll, ll, ll, ctypes.c_float, vp]
+    lib.oracle_bias_update.restype = None
     if path is None:
         _lib = lib
     return lib
@@ -61,8 +63,11 @@ def gate_logits(X_bits, Wg_bits, lib=None):
 
 
 def route(logits, k, n_micro=1, capacity_factor=1.0, capacity_override=-1,
-          alpha=0.01, renorm=False, lib=None):
+          alpha=0.01, renorm=False, select_bias=None, lib=None):
     """Route ``logits`` [T,E] (any float dtype; widened exactly to float64).
+
+    ``select_bias``: optional float32 [E] added to the logits for the expert
+    choice only (fp32 sum); weights and statistics stay unbiased.
 
     Returns a dict of numpy arrays named like the C-ABI outputs, plus
     ``capacity`` (int, -1 = unlimited).
@@ -83,7 +88,10 @@ def route(logits, k, n_micro=1, capacity_factor=1.0, capacity_override=-1,
         P=np.empty((m, E), np.float64), aux=np.empty(m, np.float64),
         cv=np.empty(m, np.float64), max_over_mean=np.empty(m, np.float64),
         extra=np.empty((m, 8), np.float64))
-    rc = lib.oracle_route(_p(L), T, E, int(k), m, C, float(alpha), int(bool(renorm)),
+    b = None if select_bias is None else np.ascontiguousarray(select_bias, dtype=np.float32)
+    if b is not None and b.shape != (E,):
+        raise ValueError("select_bias must have shape [E]")
+    rc = lib.oracle_route(_p(L), T, E, int(k), m, C, float(alpha), int(bool(renorm)), _p(b),
                           *[_p(o[n]) for n in ("topk_idx", "topk_w", "row_max", "row_sum",
                                                "counts", "offsets", "perm", "inv_perm",
                                                "dropped", "f", "P", "aux", "cv",
@@ -104,3 +112,15 @@ def backward(logits, k, counts, n_micro=1, alpha=0.01, d_aux=None, lib=None):
     out = np.empty((T, E), np.float64)
     lib.oracle_backward(_p(L), T, E, int(k), int(n_micro), float(alpha), _p(cnt), _p(g), _p(out))
     return out
+
+
+def bias_update(counts, T, k, gamma, bias, lib=None):
+    """Selection-bias step after a forward: returns the new float32 [E] bias."""
+    lib = lib or load_library()
+    cnt = np.ascontiguousarray(counts, dtype=np.int32)
+    m, E = cnt.reshape(-1, cnt.shape[-1]).shape
+    b = np.array(bias, dtype=np.float32, copy=True)
+    if b.shape != (E,):
+        raise ValueError("bias must have shape [E]")
+    lib.oracle_bias_update(_p(cnt), m, E, int(T), int(k), float(gamma), _p(b))
+    return b

@@ -14,6 +14,8 @@ Pages (address, subject, section):
        4.2 (max/min distribution ratio, entropy of the load).
   [p3] cnvsn.com/news/335486 -- load-balancing survey: 3.1/5.1 (CV = std/mean,
        balance degree 1 - (max-mean)/mean).
+  [p1] 4.3 -- loss-free balancing: a per-expert scalar bias on the router
+       logits, pushed down for overloaded experts and up for idle ones.
 """
 import itertools
 import math
@@ -380,6 +382,87 @@ def pin_gate_logits_vs_matmul(lib):
     ref = torch.matmul(torch.from_numpy(bf16_bits_to_f32(X).astype(np.float64)),
                        torch.from_numpy(bf16_bits_to_f32(W).astype(np.float64))).numpy()
     assert np.allclose(got, ref, rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------- selection bias ([p1] 4.3)
+def _fp32_sorted_order(row32, bias32):
+    """Brute-force sorted order of the fp32 sums row + bias (numpy float32
+    addition), value descending and index ascending; -0.0 == +0.0."""
+    v = (row32.astype(np.float32) + bias32.astype(np.float32)).astype(np.float32)
+    return _sorted_order_bruteforce(v.astype(np.float64))
+
+
+def pin_bias_selection_bruteforce(lib):
+    """The expert choice is the top-k of the fp32 biased logits, ties to the
+    lower index -- including ties that exist only after fp32 rounding of
+    l + b (1 + 2^-24 rounds to 1)."""
+    rng = np.random.default_rng(21)
+    for E in [2, 3, 4, 5]:
+        rows = rng.integers(-2, 3, size=(50, E)).astype(np.float32) / 2
+        bias = (rng.integers(-2, 3, size=E) / 4).astype(np.float32)
+        for k in range(1, E + 1):
+            o = _route(lib, rows, k, capacity_factor=0.0, select_bias=bias)
+            for i in range(len(rows)):
+                assert list(o["topk_idx"][i]) == _fp32_sorted_order(rows[i], bias)[:k]
+    # rounding-made tie: exact sums differ, fp32 sums are equal -> index 0
+    rows = np.array([[1.0, 1.0], [1.0, 1.0]], np.float32)
+    bias = np.array([0.0, 2.0 ** -24], np.float32)
+    o = _route(lib, rows, 1, capacity_factor=0.0, select_bias=bias)
+    assert np.all(o["topk_idx"][:, 0] == 0)
+    bias = np.array([0.0, 2.0 ** -22], np.float32)  # representable: expert 1 wins
+    o = _route(lib, rows, 1, capacity_factor=0.0, select_bias=bias)
+    assert np.all(o["topk_idx"][:, 0] == 1)
+
+
+def pin_bias_weights_and_P_unbiased(lib):
+    """The bias steers the choice only: the weights are the unbiased softmax
+    (torch, float64) at the chosen experts, P is the unbiased mean softmax,
+    and aux = alpha * E * sum f P with f from the biased choice."""
+    import torch
+    rng = np.random.default_rng(22)
+    T, E, k, alpha = 96, 12, 3, 0.02
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    bias = (0.7 * rng.standard_normal(E)).astype(np.float32)
+    o = _route(lib, L, k, capacity_factor=0.0, alpha=alpha, select_bias=bias)
+    p = torch.softmax(torch.from_numpy(L.astype(np.float64)), dim=1).numpy()
+    w = np.take_along_axis(p, o["topk_idx"].astype(np.int64), axis=1)
+    assert np.allclose(o["topk_w"], w, rtol=1e-13, atol=0)
+    assert np.allclose(o["P"][0], p.mean(0), rtol=1e-12, atol=1e-15)
+    cnt = np.bincount(o["topk_idx"].ravel(), minlength=E)
+    assert np.array_equal(o["counts"][0], cnt)
+    f = cnt / (T * k)
+    assert abs(o["aux"][0] - alpha * E * float(np.dot(f, p.mean(0)))) < 1e-12
+    # a large bias forces the choice; the weight stays the unbiased softmax
+    b2 = np.zeros(E, np.float32)
+    b2[3], b2[0] = 1.0e3, -1.0e3
+    o2 = _route(lib, L, 1, capacity_factor=0.0, select_bias=b2)
+    assert np.all(o2["topk_idx"][:, 0] == 3)
+    assert np.allclose(o2["topk_w"][:, 0], p[:, 3], rtol=1e-13, atol=0)
+    o3 = _route(lib, L, k, capacity_factor=0.0, select_bias=b2)
+    assert not np.any(o3["topk_idx"] == 0)
+
+
+def pin_bias_update_rule(lib):
+    """Loads summed over microbatches against the mean T*k/E: overloaded
+    experts step down by gamma, idle ones up, balanced ones stay -- each step
+    the fp32 operation numpy performs."""
+    b = oracle.bias_update(np.array([[5, 3, 4, 4]]), T=8, k=2, gamma=0.5,
+                           bias=np.zeros(4, np.float32), lib=lib)
+    assert list(b) == [-0.5, 0.5, 0.0, 0.0]
+    # two microbatches, mean 10/3 (not an integer): [4,3,3] is over, under, under
+    cnt = np.array([[2, 2, 1], [2, 1, 2]])
+    b = oracle.bias_update(cnt, T=5, k=2, gamma=0.25, bias=np.array([1, 1, 1], np.float32), lib=lib)
+    assert list(b) == [0.75, 1.25, 1.25]
+    # fp32 steps: compare with numpy float32 arithmetic
+    rng = np.random.default_rng(23)
+    E, T, k, m = 37, 400, 3, 4
+    cnt = rng.multinomial(T // m * k, np.ones(E) / E, size=m).astype(np.int32)
+    b0 = (1e3 * rng.standard_normal(E)).astype(np.float32)
+    g = np.float32(0.001)
+    load = cnt.sum(0)
+    want = np.where(load * E > T * k, b0 - g, np.where(load * E < T * k, b0 + g, b0)).astype(np.float32)
+    got = oracle.bias_update(cnt, T=T, k=k, gamma=float(g), bias=b0, lib=lib)
+    assert np.array_equal(got, want)
 
 
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

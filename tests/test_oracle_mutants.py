@@ -54,6 +54,13 @@ MUTANTS = {
     "entropy_log2": ("ent -= fe * log(fe);", "ent -= fe * log2(fe);"),
     "balance_degree_sign": ("x[1] = 1.0 - (cmax - mean) / mean;",
                             "x[1] = 1.0 + (cmax - mean) / mean;"),
+    "bias_ignored": ("topk_row(selrow, E, k, idx, taken);",
+                     "topk_row(row, E, k, idx, taken);"),
+    "bias_added_in_double": ("selrow[e] = (double)biased;",
+                             "selrow[e] = row[e] + (double)select_bias[e]; (void)biased;"),
+    "bias_update_sign": ("bias[e] = bias[e] - gamma;", "bias[e] = bias[e] + gamma;"),
+    "bias_update_first_mb_only": ("for (long long mb = 0; mb < n_micro; ++mb)\n            load += counts[mb * E + e];",
+                                  "load += counts[e] * n_micro;"),
 }
 
 
