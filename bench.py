@@ -83,6 +83,10 @@ def alg_bytes(w, T):
     scatter = 5 * T * k
     bwd = (8 * T * E + 8 * T) if w.backward else 0
     forward = (gate + 8 * T * k + stats + scatter) if d > 0 else (rows + scatter)
+    if w.select_bias_scale > 0:
+        # selection bias read by the row pass; the update reads the counts
+        # and reads and writes the bias
+        forward += 4 * E + (4 * w.n_micro * E + 8 * E if w.bias_gamma > 0 else 0)
     return {"rows": rows, "gate": gate, "scatter": scatter, "backward": bwd, "forward": forward}
 
 
@@ -134,9 +138,11 @@ def cpu_baseline(w, inp, budget_s):
         else:
             lg = oracle.gate_logits(X[:n], Wg)
         o = oracle.route(lg, w.k, n_micro=m, capacity_factor=w.capacity_factor, alpha=w.alpha,
-                         renorm=w.renorm)
+                         renorm=w.renorm, select_bias=inp.get("select_bias"))
         if w.backward:
             oracle.backward(lg, w.k, o["counts"], n_micro=m, alpha=w.alpha)
+        if w.bias_gamma > 0:
+            oracle.bias_update(o["counts"], T=n, k=w.k, gamma=w.bias_gamma, bias=inp["select_bias"])
         return time.perf_counter() - t0
 
     t_small = run(n0)
@@ -150,7 +156,9 @@ def cpu_baseline(w, inp, budget_s):
             break
     sample = (f"oracle (serial C, fp64) on the first {n} tokens of the seed-0 {w.name} inputs"
               f" x{reps} pass(es): forward" + (" + backward" if w.backward else "")
-              + (" incl. gate GEMM" if w.d > 0 else ""))
+              + (" incl. gate GEMM" if w.d > 0 else "")
+              + (" with selection bias" if w.select_bias_scale > 0 else "")
+              + (" + bias update" if w.bias_gamma > 0 else ""))
     return {"value": tokens / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": sample, "seconds": round(elapsed, 2)}
 
@@ -173,7 +181,8 @@ def main():
     inp = make_inputs(w, 0)
     p = lbs.make_params(w.T, w.E, w.k, n_micro=w.n_micro, d=w.d,
                         capacity_factor=w.capacity_factor, alpha=w.alpha, renorm=w.renorm,
-                        save_row_stats=w.backward)
+                        save_row_stats=w.backward, select_bias=w.select_bias_scale > 0)
+    sbias = (torch.from_numpy(inp["select_bias"]).to(dev) if w.select_bias_scale > 0 else None)
     # input copies for cache rotation
     if w.d > 0:
         X0 = torch.from_numpy(inp["X"].view(np.int16)).to(dev)
@@ -200,7 +209,10 @@ def main():
     def step(i, timed):
         src = srcs[i % ncopy]
         kw = dict(X=src, Wg=Wg) if w.d > 0 else dict(logits=src)
-        lbs.moe_route(p, out, ws, stream=stream, row_pass_events=ev_rows[i] if timed else None, **kw)
+        lbs.moe_route(p, out, ws, stream=stream, row_pass_events=ev_rows[i] if timed else None,
+                      select_bias=sbias, **kw)
+        if w.bias_gamma > 0:  # one loss-free balancing step: the bias follows the loads
+            lbs.moe_route_bias_update(p, out["counts"], w.bias_gamma, sbias, stream=stream)
         if w.backward:
             L = out["logits"] if w.d > 0 else src
             if timed:
@@ -283,7 +295,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "T": w.T, "E": w.E, "k": w.k, "n_micro": w.n_micro,
                    "d": w.d, "capacity_factor": w.capacity_factor, "alpha": w.alpha,
-                   "renorm": w.renorm, "backward": w.backward},
+                   "renorm": w.renorm, "backward": w.backward,
+                   "select_bias": w.select_bias_scale > 0, "bias_gamma": w.bias_gamma},
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "alg_bytes_per_launch": dom_bytes,

@@ -13,6 +13,8 @@
  *        only in training), 4.2 (distribution ratio, entropy of the load).
  *   [p3] cnvsn.com/news/335486 -- load-balancing survey: 3.1 and 5.1
  *        (coefficient of variation, load-balance degree).
+ *   [p1] 4.3 -- loss-free balancing: a per-expert scalar bias on the router
+ *        logits, moved down for overloaded experts and up for idle ones.
  *
  * Conventions shared by every entry point:
  *   - Every array pointer is a DEVICE pointer to memory that the caller
@@ -52,6 +54,7 @@ extern "C" {
 #define MOE_RENORM_TOPK    1u /* rescale the k gate weights to sum to 1     */
 #define MOE_SAVE_ROW_STATS 2u /* write per-token softmax (max, sum)         */
 #define MOE_WRITE_INV_PERM 4u /* write inv_perm                             */
+#define MOE_SELECT_BIAS    8u /* moe_route's select_bias [E] steers the choice */
 
 /* Bits of the optional status word (set for the whole call). */
 #define MOE_STATUS_NONFINITE 1 /* a row had a NaN/+inf logit, or only -inf;
@@ -143,14 +146,33 @@ int moe_route_capacity(const moe_route_params *p, int32_t *capacity);
  * Forward routing ([p1] 4.2-4.5, [p2] 2.2, [p3] 3.1/5.1).
  * logits [T,E] fp32 when p->d == 0 (X, Wg ignored); when p->d > 0, X [T,d]
  * and Wg [d,E] are bf16 bit patterns (uint16) and out->logits receives
- * X.Wg accumulated in fp32 (logits ignored).  Enqueues the whole forward on
- * stream.  workspace: device buffer of at least moe_route_workspace_size()
- * bytes, used only during the call's kernels (calls sharing one workspace
- * must be ordered on one stream).
+ * X.Wg accumulated in fp32 (logits ignored).
+ * select_bias [E] fp32: required when MOE_SELECT_BIAS is set, ignored
+ * otherwise.  [p1] 4.3: the per-expert bias b_e is added to the logits to
+ * steer the expert choice; here it enters the choice only -- experts are
+ * ranked by the fp32 sum l + b_e (ties to the lower expert) while the gate
+ * weights, P and the aux loss use the unbiased softmax.
+ * Enqueues the whole forward on stream.  workspace: device buffer of at
+ * least moe_route_workspace_size() bytes, used only during the call's
+ * kernels (calls sharing one workspace must be ordered on one stream).
  */
 int moe_route(const moe_route_params *p, const float *logits, const uint16_t *X,
-              const uint16_t *Wg, const moe_route_out *out, void *workspace,
-              size_t workspace_bytes, void *stream);
+              const uint16_t *Wg, const float *select_bias, const moe_route_out *out,
+              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One update of the selection bias after a forward ([p1] 4.3: an overloaded
+ * expert's bias is pushed down, an idle expert's up, with no loss term).
+ * The page fixes no step form; this is a fixed step against the sign of the
+ * load error, in fp32:
+ *   load_e = sum over microbatches of counts[mb][e];
+ *   bias[e] -= gamma if load_e * E > T * k;  bias[e] += gamma if
+ *   load_e * E < T * k;  unchanged if equal (exact integer comparison).
+ * counts [m,E] int32: the forward's counts; bias [E] fp32: updated in
+ * place.  Uses p->T, E, k, n_micro only.  gamma must be finite and >= 0.
+ */
+int moe_route_bias_update(const moe_route_params *p, const int32_t *counts, float gamma,
+                          float *bias, void *stream);
 
 /*
  * Gradient of the aux loss with respect to the logits ([p1] 4.2: f carries

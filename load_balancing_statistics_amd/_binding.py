@@ -20,6 +20,7 @@ MOE_ERR_HIP = -4
 MOE_RENORM_TOPK = 1
 MOE_SAVE_ROW_STATS = 2
 MOE_WRITE_INV_PERM = 4
+MOE_SELECT_BIAS = 8
 
 MOE_STATUS_NONFINITE = 1
 MOE_STATUS_INTERNAL = 2
@@ -76,10 +77,12 @@ def load(path=None):
     lib.moe_route_workspace_size.restype = ctypes.c_int
     lib.moe_route_capacity.argtypes = [P, ctypes.POINTER(ctypes.c_int32)]
     lib.moe_route_capacity.restype = ctypes.c_int
-    lib.moe_route.argtypes = [P, vp, vp, vp, ctypes.POINTER(moe_route_out), vp, ctypes.c_size_t, vp]
+    lib.moe_route.argtypes = [P, vp, vp, vp, vp, ctypes.POINTER(moe_route_out), vp, ctypes.c_size_t, vp]
     lib.moe_route.restype = ctypes.c_int
     lib.moe_route_backward.argtypes = [P, vp, vp, vp, vp, vp, vp]
     lib.moe_route_backward.restype = ctypes.c_int
+    lib.moe_route_bias_update.argtypes = [P, vp, ctypes.c_float, vp, vp]
+    lib.moe_route_bias_update.restype = ctypes.c_int
     lib.moe_route_strerror.argtypes = [ctypes.c_int]
     lib.moe_route_strerror.restype = ctypes.c_char_p
     if path is None:
@@ -88,9 +91,9 @@ def load(path=None):
 
 
 def make_params(T, E, k, n_micro=1, d=0, capacity_factor=1.0, capacity=-1, alpha=0.01,
-                renorm=False, save_row_stats=False, inv_perm=False):
+                renorm=False, save_row_stats=False, inv_perm=False, select_bias=False):
     flags = ((MOE_RENORM_TOPK if renorm else 0) | (MOE_SAVE_ROW_STATS if save_row_stats else 0)
-             | (MOE_WRITE_INV_PERM if inv_perm else 0))
+             | (MOE_WRITE_INV_PERM if inv_perm else 0) | (MOE_SELECT_BIAS if select_bias else 0))
     return moe_route_params(int(T), int(E), int(k), int(n_micro), int(d), float(capacity_factor),
                             int(capacity), float(alpha), flags)
 
@@ -127,8 +130,11 @@ def moe_route_capacity(params):
 
 
 def moe_route(params, out, workspace, logits=None, X=None, Wg=None, stream=None,
-              row_pass_events=None):
+              row_pass_events=None, select_bias=None):
     """Forward routing; ``out`` maps output names to device tensors (or None).
+
+    ``select_bias``: fp32 [E] device tensor, used when the params carry
+    MOE_SELECT_BIAS (expert choice on logits + bias, weights unbiased).
 
     ``row_pass_events``: optional pair of raw hipEvent_t handles (ints) that the
     library records around the row-pass kernel."""
@@ -136,7 +142,8 @@ def moe_route(params, out, workspace, logits=None, X=None, Wg=None, stream=None,
     if row_pass_events is not None:
         o.row_pass_events[0] = row_pass_events[0]
         o.row_pass_events[1] = row_pass_events[1]
-    rc = load().moe_route(ctypes.byref(params), _ptr(logits), _ptr(X), _ptr(Wg), ctypes.byref(o),
+    rc = load().moe_route(ctypes.byref(params), _ptr(logits), _ptr(X), _ptr(Wg), _ptr(select_bias),
+                          ctypes.byref(o),
                           _ptr(workspace), workspace.numel() * workspace.element_size()
                           if workspace is not None else 0, _stream(stream))
     if rc != MOE_OK:
@@ -149,6 +156,14 @@ def moe_route_backward(params, logits, counts, dlogits, row_stats=None, d_aux=No
                                    _ptr(counts), _ptr(d_aux), _ptr(dlogits), _stream(stream))
     if rc != MOE_OK:
         raise MoeRouteError(rc, "moe_route_backward")
+
+
+def moe_route_bias_update(params, counts, gamma, bias, stream=None):
+    """One selection-bias step from the forward's counts; ``bias`` is updated in place."""
+    rc = load().moe_route_bias_update(ctypes.byref(params), _ptr(counts), float(gamma), _ptr(bias),
+                                      _stream(stream))
+    if rc != MOE_OK:
+        raise MoeRouteError(rc, "moe_route_bias_update")
 
 
 def alloc_outputs(params, device="cuda"):

@@ -12,7 +12,7 @@ namespace {
 
 using moe::RowCfg;
 
-constexpr uint32_t kKnownFlags = MOE_RENORM_TOPK | MOE_SAVE_ROW_STATS | MOE_WRITE_INV_PERM;
+constexpr uint32_t kKnownFlags = MOE_RENORM_TOPK | MOE_SAVE_ROW_STATS | MOE_WRITE_INV_PERM | MOE_SELECT_BIAS;
 constexpr size_t kMaxLds = 160 * 1024;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -27,10 +27,15 @@ int check_shape(const moe_route_params* p) {
     if (p->capacity < -1) return MOE_ERR_INVALID_ARG;
     if (p->flags & ~kKnownFlags) return MOE_ERR_INVALID_ARG;
     if (p->d > 0 && !moe::gate_supported(p->T, p->d, p->E)) return MOE_ERR_UNSUPPORTED;
-    const RowCfg c = moe::choose_rows(p->T, p->E, p->k, p->n_micro);
-    if (c.G < 0 || moe::rows_lds_bytes(c, p->E, p->k) > kMaxLds) return MOE_ERR_UNSUPPORTED;
+    const bool bias = (p->flags & MOE_SELECT_BIAS) != 0;
+    const RowCfg c = moe::choose_rows(p->T, p->E, p->k, p->n_micro, bias);
+    if (c.G < 0 || moe::rows_lds_bytes(c, p->E, p->k, bias) > kMaxLds) return MOE_ERR_UNSUPPORTED;
     if (moe::scatter_lds_bytes(p->E, p->k) > kMaxLds) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
+}
+
+RowCfg cfg_of(const moe_route_params* p) {
+    return moe::choose_rows(p->T, p->E, p->k, p->n_micro, (p->flags & MOE_SELECT_BIAS) != 0);
 }
 
 int64_t capacity_of(const moe_route_params* p) {
@@ -85,7 +90,7 @@ int moe_route_workspace_size(const moe_route_params* p, size_t* bytes) {
     const int rc = check_shape(p);
     if (rc != MOE_OK) return rc;
     if (!bytes) return MOE_ERR_INVALID_ARG;
-    *bytes = workspace_bytes(p, moe::choose_rows(p->T, p->E, p->k, p->n_micro));
+    *bytes = workspace_bytes(p, cfg_of(p));
     return MOE_OK;
 }
 
@@ -98,8 +103,8 @@ int moe_route_capacity(const moe_route_params* p, int32_t* capacity) {
 }
 
 int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
-              const uint16_t* Wg, const moe_route_out* out, void* workspace,
-              size_t workspace_bytes_given, void* stream) {
+              const uint16_t* Wg, const float* select_bias, const moe_route_out* out,
+              void* workspace, size_t workspace_bytes_given, void* stream) {
     int rc = check_shape(p);
     if (rc != MOE_OK) return rc;
     if (!out) return MOE_ERR_INVALID_ARG;
@@ -115,13 +120,15 @@ int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
         return MOE_ERR_INVALID_ARG;
     if ((p->flags & MOE_SAVE_ROW_STATS) && !out->row_stats) return MOE_ERR_INVALID_ARG;
     if ((p->flags & MOE_WRITE_INV_PERM) && !out->inv_perm) return MOE_ERR_INVALID_ARG;
+    const bool bias = (p->flags & MOE_SELECT_BIAS) != 0;
+    if (bias && (!select_bias || !aligned(select_bias, 4))) return MOE_ERR_INVALID_ARG;
     const void* fptrs[] = {out->topk_idx, out->topk_w, out->row_stats, out->counts, out->offsets,
                            out->perm, out->inv_perm, out->f, out->P, out->aux_loss, out->cv,
                            out->max_over_mean, out->extra_stats, out->status};
     for (const void* q : fptrs)
         if (q && !aligned(q, 4)) return MOE_ERR_INVALID_ARG;
 
-    const RowCfg c = moe::choose_rows(p->T, p->E, p->k, p->n_micro);
+    const RowCfg c = cfg_of(p);
     const size_t need = workspace_bytes(p, c);
     if (!workspace || workspace_bytes_given < need || !aligned(workspace, 256)) return MOE_ERR_WORKSPACE;
     const moe::Workspace ws = moe::carve_workspace(
@@ -138,6 +145,7 @@ int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
 
     moe::RowsArgs ra{};
     ra.logits = L;
+    ra.bias = bias ? select_bias : nullptr;
     ra.T = p->T; ra.E = p->E; ra.k = p->k; ra.Tm = Tm; ra.R = c.R; ra.bpm = c.bpm;
     ra.renorm = (p->flags & MOE_RENORM_TOPK) ? 1 : 0;
     ra.save_stats = (p->flags & MOE_SAVE_ROW_STATS) ? 1 : 0;
@@ -193,6 +201,21 @@ int moe_route_backward(const moe_route_params* p, const float* logits, const flo
     b.T = q.T; b.E = q.E; b.k = q.k; b.Tm = q.T / q.n_micro; b.R = c.R; b.bpm = c.bpm;
     b.alpha = q.alpha;
     if (moe::launch_route_backward(c, b, static_cast<hipStream_t>(stream)) != hipSuccess) return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+int moe_route_bias_update(const moe_route_params* p, const int32_t* counts, float gamma,
+                          float* bias, void* stream) {
+    if (!p) return MOE_ERR_INVALID_ARG;
+    moe_route_params q = *p;
+    q.d = 0;
+    q.flags = 0;
+    const int rc = check_shape(&q);
+    if (rc != MOE_OK) return rc;
+    if (!counts || !bias || !aligned(counts, 4) || !aligned(bias, 4)) return MOE_ERR_INVALID_ARG;
+    if (!std::isfinite(gamma) || gamma < 0.f) return MOE_ERR_INVALID_ARG;
+    moe::BiasArgs b{counts, bias, q.E, q.n_micro, int64_t(q.T) * q.k, gamma};
+    if (moe::launch_bias_update(b, static_cast<hipStream_t>(stream)) != hipSuccess) return MOE_ERR_HIP;
     return MOE_OK;
 }
 

@@ -45,7 +45,7 @@ inline int next_pow2(int v) {
 // per-lane column count fits the table.  Then the rows per block: about two
 // or three resident blocks per compute unit over the whole batch, so the
 // grid is one wave of blocks and the per-block partials stay few.
-inline RowCfg choose_rows(int T, int E, int k, int n_micro) {
+inline RowCfg choose_rows(int T, int E, int k, int n_micro, bool bias = false) {
     RowCfg c{};
     c.VEC = (E % 4 == 0) ? 4 : 1;
     int S = next_pow2(k < 1 ? 1 : k);
@@ -63,7 +63,9 @@ inline RowCfg choose_rows(int T, int E, int k, int n_micro) {
     // One block per compute unit holding as many waves as the row pass's
     // registers allow: 16 (4 per SIMD) when a lane owns up to 16 columns,
     // 12 when it owns 24.
-    c.NW = (c.G > 16) ? 12 : 16;
+    // The selection-bias variant keeps G more registers per lane: 12 waves
+    // when a lane owns up to 16 columns, 8 when it owns 24.
+    c.NW = bias ? ((c.G > 16) ? 8 : 12) : ((c.G > 16) ? 12 : 16);
     const int W = 64 / S;
     const long per_iter = long(c.NW) * W;
     const long Tm = T / n_micro;
@@ -115,9 +117,9 @@ inline int rows_queue_cap(const RowCfg& c) {
     return ((c.R + per_iter - 1) / per_iter) * W;
 }
 
-inline size_t rows_lds_bytes(const RowCfg& c, int E, int k) {
+inline size_t rows_lds_bytes(const RowCfg& c, int E, int k, bool bias = false) {
     const int W = 64 / c.S;
-    size_t hist = align_up(size_t(E) * 4, 16);
+    size_t hist = align_up(size_t(E) * 4, 16) * (bias ? 2 : 1);
     size_t rowbuf = size_t(c.NW) * W * row_stride(c.S, c.G) * 4;
     size_t cand = size_t(c.NW) * W * cand_stride(c.S, c.G) * 8;
     size_t sel = size_t(c.NW) * W * k * 8;
@@ -173,6 +175,7 @@ inline Workspace carve_workspace(void* base, const RowCfg& c, int E, int m, size
 // ------------------------------------------------------- kernel arguments
 struct RowsArgs {
     const float* logits;
+    const float* bias;  // [E] selection bias, or nullptr
     int T, E, k, Tm, R, bpm;
     int renorm, save_stats;
     int qcap;  // per-wave queue entries: row groups of the largest block times rows per group
@@ -233,6 +236,14 @@ struct BackArgs {
     float alpha;
 };
 
+struct BiasArgs {
+    const int32_t* counts;  // [m,E]
+    float* bias;            // [E], updated in place
+    int E, n_micro;
+    int64_t Tk;             // T * k
+    float gamma;
+};
+
 struct GateArgs {
     const uint16_t* X;
     const uint16_t* Wg;
@@ -257,6 +268,7 @@ hipError_t launch_route_scatter(const RowCfg& c, const ScatterArgs& a, hipStream
 int scatter_rows_per_wave(int E, int k);
 size_t scatter_lds_bytes(int E, int k);
 hipError_t launch_route_backward(const RowCfg& c, const BackArgs& a, hipStream_t st);
+hipError_t launch_bias_update(const BiasArgs& a, hipStream_t st);
 hipError_t launch_gate_gemm(const GateArgs& a, uint16_t* wt, hipStream_t st);
 bool gate_supported(int T, int d, int E);
 size_t gate_workspace_bytes(int d, int E);

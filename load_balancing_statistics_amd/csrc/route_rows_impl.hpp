@@ -12,6 +12,12 @@
 //     experts), optionally renormalised over the k picks;
 //   * the block's expert histogram (LDS integer atomics) and the block's
 //     per-expert sums of softmax probabilities, used for f_i and P_i.
+// With a selection bias (BIAS; page mhpq.cn/news/998159 section 4.3) the
+// experts are ranked by the fp32 sums l + b_e while the softmax, the weights
+// and the probability sums use l: each lane keeps the bias of its columns in
+// registers (threshold and candidate mask) and the block keeps a copy in LDS
+// (candidate keys); the LDS row copy stays unbiased, so a winner's weight
+// is read from it exactly.
 //
 // Top-k without sorting.  Lane s of a segment owns G columns.  The k-th
 // largest of the S lane maxima, tau, is a lower bound of the row's k-th
@@ -85,7 +91,7 @@ __device__ __forceinline__ void load_row(float (&x)[G], const float* __restrict_
     }
 }
 
-template <int S, int G, int VEC, bool PAD, int NW>
+template <int S, int G, int VEC, bool PAD, int NW, bool BIAS>
 struct RowPass {
     static constexpr int W = 64 / S;               // rows per wave at a time
     static constexpr int RS = row_stride(S, G);    // LDS row-copy stride (floats)
@@ -96,14 +102,15 @@ struct RowPass {
     // Exact top-k of a row from its LDS copy: k rounds of arg-max of the
     // order keys over the segment (rows whose candidate list overflows).
     __device__ __forceinline__ static void fallback_select(
-        const float* rowbuf, uint64_t* sel, int E, int k, int s) {
+        const float* rowbuf, const float* blds, uint64_t* sel, int E, int k, int s) {
         uint64_t prev = ~0ull;
         for (int j = 0; j < k; ++j) {
             uint64_t best = 0;
             for (int g = 0; g < G; ++g) {
                 const int col = col_of<S, VEC>(g, s);
                 if (!PAD || col < E) {
-                    const uint64_t key = make_key(rowbuf[col], col);
+                    const float v = BIAS ? rowbuf[col] + blds[col] : rowbuf[col];
+                    const uint64_t key = make_key(v, col);
                     if (key < prev && key > best) best = key;
                 }
             }
@@ -127,29 +134,37 @@ struct RowPass {
     __device__ __forceinline__ static void process(
         const RowsArgs& a, const float (&x)[G], long row, bool valid, int s,
         float* rowbuf, uint64_t* cand, int* hist, float (&acc)[G], int& bad,
-        int* queue, int& qn, long row_begin)
+        int* queue, int& qn, long row_begin, const float (&bz)[G], const float* blds)
     {
         const int E = a.E, k = a.k;
-        // ---- row maximum and the candidate threshold tau
+        // ---- row maximum (softmax) and the candidate threshold tau
+        // (selection values: the logits, or the biased logits)
         float lmax = x[0];
 #pragma unroll
         for (int g = 1; g < G; ++g) lmax = fmaxf(lmax, x[g]);
         const float m = seg_max<S>(lmax);
-        float tau = m;
+        float ymax = lmax;
+        if constexpr (BIAS) {
+            ymax = x[0] + bz[0];
+#pragma unroll
+            for (int g = 1; g < G; ++g) ymax = fmaxf(ymax, x[g] + bz[g]);
+        }
+        float tau = BIAS ? seg_max<S>(ymax) : m;
         if constexpr (S > 1) {
             if (k > 1) {
-                const int ge = count_ge<S, 1>(lmax);
+                const int ge = count_ge<S, 1>(ymax);
                 // the largest lane maximum reached by at least k lane maxima
-                tau = seg_max<S>(ge >= k ? lmax : -INFINITY);
+                tau = seg_max<S>(ge >= k ? ymax : -INFINITY);
             }
         }
 
-        // ---- candidates x >= tau (bit g of mask), real columns only
+        // ---- candidates y >= tau (bit g of mask), real columns only
         unsigned mask = 0;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
             const bool real = !PAD || col_of<S, VEC>(g, s) < E;
-            mask |= (x[g] >= tau && real) ? (1u << g) : 0u;
+            const float y = BIAS ? x[g] + bz[g] : x[g];
+            mask |= (y >= tau && real) ? (1u << g) : 0u;
         }
         if (!valid) mask = 0;
         const int n = __popc(mask);
@@ -177,7 +192,7 @@ struct RowPass {
             ecol[u] = col_from_bit(g, s);
         }
 #pragma unroll
-        for (int u = 0; u < XB; ++u) ev[u] = rowbuf[ecol[u]];
+        for (int u = 0; u < XB; ++u) ev[u] = BIAS ? rowbuf[ecol[u]] + blds[ecol[u]] : rowbuf[ecol[u]];
 
         // ---- softmax statistics and probability sums (hides the reads)
         const float mL = m * kLog2e;
@@ -225,7 +240,7 @@ struct RowPass {
                     const int g = __ffs(mm) - 1;
                     mm &= mm - 1;
                     const int col = col_from_bit(g, s);
-                    cand[o2++] = make_key(rowbuf[col], col);
+                    cand[o2++] = make_key(BIAS ? rowbuf[col] + blds[col] : rowbuf[col], col);
                 }
             }
             // pad the list to a multiple of 4 keys
@@ -250,7 +265,8 @@ struct RowPass {
                     if (c < C && rank < k) {
                         wrank[p] = rank;
                         wcol[p] = key_col(my);
-                        we[p] = __builtin_amdgcn_exp2f(fmaf(key_val(my), kLog2e, -mL));
+                        const float lv = BIAS ? rowbuf[wcol[p]] : key_val(my);
+                        we[p] = __builtin_amdgcn_exp2f(fmaf(lv, kLog2e, -mL));
                     }
                 }
             }
@@ -282,7 +298,7 @@ struct RowPass {
     // accumulated by the streaming pass.
     __device__ __forceinline__ static void resolve_queue(
         const RowsArgs& a, const int* queue, int qn, long row_begin, int s, int seg,
-        float* rowbuf, uint64_t* sel, int* hist)
+        float* rowbuf, uint64_t* sel, int* hist, const float* blds)
     {
         const int E = a.E, k = a.k;
         for (int q0 = 0; q0 < qn; q0 += W) {
@@ -301,13 +317,14 @@ struct RowPass {
             ssum = seg_sum<S>(ssum);
 #pragma unroll
             for (int g = 0; g < G; ++g) rowbuf[col_of<S, VEC>(g, s)] = x[g];
-            fallback_select(rowbuf, sel, E, k, s);
+            fallback_select(rowbuf, blds, sel, E, k, s);
             float e = 0.f;
             int col = 0;
             if (s < k) {
                 const uint64_t key = sel[s];
                 col = key_col(key);
-                e = __builtin_amdgcn_exp2f(fmaf(key_val(key), kLog2e, -mL));
+                const float lv = BIAS ? rowbuf[col] : key_val(key);
+                e = __builtin_amdgcn_exp2f(fmaf(lv, kLog2e, -mL));
             }
             const float rden = a.renorm ? __builtin_amdgcn_rcpf(seg_sum<S>(s < k ? e : 0.f))
                                         : __builtin_amdgcn_rcpf(ssum);
@@ -320,17 +337,19 @@ struct RowPass {
     }
 };
 
-template <int S, int G, int VEC, bool PAD, int NW>
+template <int S, int G, int VEC, bool PAD, int NW, bool BIAS>
 __global__ void __launch_bounds__(NW * 64)
 route_rows_kernel(const RowsArgs a)
 {
-    using RP = RowPass<S, G, VEC, PAD, NW>;
+    using RP = RowPass<S, G, VEC, PAD, NW, BIAS>;
     constexpr int W = RP::W, RS = RP::RS, CS = RP::CS;
 
     extern __shared__ __align__(16) unsigned char smem[];
     const int E = a.E, k = a.k;
     int* hist = reinterpret_cast<int*>(smem);
-    float* rowbuf_all = reinterpret_cast<float*>(smem + ((E * 4 + 15) & ~15));
+    float* blds = reinterpret_cast<float*>(smem + ((E * 4 + 15) & ~15));  // [E] when BIAS
+    float* rowbuf_all = reinterpret_cast<float*>(
+        reinterpret_cast<unsigned char*>(blds) + (BIAS ? ((E * 4 + 15) & ~15) : 0));
     uint64_t* cand_all = reinterpret_cast<uint64_t*>(
         reinterpret_cast<unsigned char*>(rowbuf_all) + ((NW * W * RS * 4 + 15) & ~15));
     uint64_t* sel_all = cand_all + NW * W * CS;
@@ -343,6 +362,8 @@ route_rows_kernel(const RowsArgs a)
     block_rows(blockIdx.x, a.bpm, a.Tm, row_begin, row_end);
 
     for (int e = tid; e < E; e += NW * 64) hist[e] = 0;
+    if constexpr (BIAS)
+        for (int e = tid; e < E; e += NW * 64) blds[e] = a.bias[e];
     if (blockIdx.x == 0)
         for (int m = tid; m < a.n_micro; m += NW * 64) a.arrive[m] = 0;
     __syncthreads();
@@ -357,6 +378,17 @@ route_rows_kernel(const RowsArgs a)
 #pragma unroll
     for (int g = 0; g < G; ++g) acc[g] = 0.f;
     int bad = 0;
+    // bias of the lane's columns (0 for padding columns; unused without BIAS)
+    float bz[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) bz[g] = 0.f;
+    if constexpr (BIAS) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int col = col_of<S, VEC>(g, s);
+            if (!PAD || col < E) bz[g] = a.bias[col];
+        }
+    }
 
     const long per_iter = long(NW) * W;
     const int iters = int((row_end - row_begin + per_iter - 1) / per_iter);
@@ -372,22 +404,22 @@ route_rows_kernel(const RowsArgs a)
     int it = 0;
     for (; it + 2 < iters; it += 2) {
         load_row<S, G, VEC, PAD>(xb, a.logits, clamp(row_at(it + 1)), E, s);
-        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin);
+        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin, bz, blds);
         load_row<S, G, VEC, PAD>(xa, a.logits, clamp(row_at(it + 2)), E, s);
         RP::process(a, xb, row_at(it + 1), row_at(it + 1) < row_end, s, rowbuf, cand, hist,
-                    acc, bad, queue, qn, row_begin);
+                    acc, bad, queue, qn, row_begin, bz, blds);
     }
     if (it + 1 < iters) {
         load_row<S, G, VEC, PAD>(xb, a.logits, clamp(row_at(it + 1)), E, s);
-        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin);
+        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin, bz, blds);
         RP::process(a, xb, row_at(it + 1), row_at(it + 1) < row_end, s, rowbuf, cand, hist,
-                    acc, bad, queue, qn, row_begin);
+                    acc, bad, queue, qn, row_begin, bz, blds);
     } else if (it < iters) {
-        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin);
+        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin, bz, blds);
     }
 
     if (__builtin_expect(qn > 0, 0))
-        RP::resolve_queue(a, queue, qn, row_begin, s, seg, rowbuf, sel, hist);
+        RP::resolve_queue(a, queue, qn, row_begin, s, seg, rowbuf, sel, hist, blds);
 
     // ---- block partials: probability sums (fixed order) and histogram.
     // Lanes with the same s in different segments own the same columns.
@@ -506,10 +538,10 @@ route_backward_kernel(const BackArgs a)
     }
 }
 
-template <int S, int G, int VEC, bool PAD, int NW>
+template <int S, int G, int VEC, bool PAD, int NW, bool BIAS>
 hipError_t launch_rows_nw(const RowCfg& c, const RowsArgs& a, hipStream_t st) {
-    const size_t lds = rows_lds_bytes(c, a.E, a.k);
-    auto kern = route_rows_kernel<S, G, VEC, PAD, NW>;
+    const size_t lds = rows_lds_bytes(c, a.E, a.k, BIAS);
+    auto kern = route_rows_kernel<S, G, VEC, PAD, NW, BIAS>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
@@ -521,8 +553,13 @@ hipError_t launch_rows_nw(const RowCfg& c, const RowsArgs& a, hipStream_t st) {
 
 template <int S, int G, int VEC, bool PAD>
 hipError_t launch_rows(const RowCfg& c, const RowsArgs& a, hipStream_t st) {
-    if (c.NW == 16) return launch_rows_nw<S, G, VEC, PAD, 16>(c, a, st);
-    if (c.NW == 12) return launch_rows_nw<S, G, VEC, PAD, 12>(c, a, st);
+    if (a.bias) {
+        if (c.NW == 12) return launch_rows_nw<S, G, VEC, PAD, 12, true>(c, a, st);
+        if (c.NW == 8) return launch_rows_nw<S, G, VEC, PAD, 8, true>(c, a, st);
+        return hipErrorInvalidValue;
+    }
+    if (c.NW == 16) return launch_rows_nw<S, G, VEC, PAD, 16, false>(c, a, st);
+    if (c.NW == 12) return launch_rows_nw<S, G, VEC, PAD, 12, false>(c, a, st);
     return hipErrorInvalidValue;
 }
 

@@ -21,9 +21,13 @@ Workloads (T tokens, E experts, top-k, m microbatches):
 * ``v4_shape``   -- 16 microbatches of 16384 tokens, E=384, top-6; logits
   N(0,1) with a fresh random hot set of 16 experts per microbatch boosted by
   +2.0; capacity factor 1.0, forward plus aux-loss backward.
+* ``v3_select_bias`` -- the v3 shape routed the loss-free way: logits iid
+  N(0,1) and a separate per-expert selection bias N(0, 0.5^2) that steers
+  the expert choice only, alpha 0 (no aux loss), followed by one bias update
+  step (gamma 0.001).
 
 Draw order for a seed: per-expert bias or hot sets first, then the logits
-(for the gate workload: X, then Wg).
+(for the gate workload: X, then Wg), then the selection bias if any.
 """
 from dataclasses import dataclass, replace
 
@@ -43,6 +47,8 @@ class Workload:
     d: int = 0             # 0: logits given; > 0: gate GEMM with hidden size d
     backward: bool = False # the workload also runs the aux-loss backward
     logits_kind: str = "normal"  # normal | zipf_bias | normal_bias | hot_set
+    select_bias_scale: float = 0.0  # > 0: a selection bias N(0, scale^2) per expert
+    bias_gamma: float = 0.0         # step of the bias update that follows the forward
 
     @property
     def Tm(self):
@@ -72,6 +78,9 @@ WORKLOADS = {
     "v4_shape": Workload("v4_shape", T=262144, E=384, k=6, n_micro=16,
                          capacity_factor=1.0, alpha=0.01, renorm=True,
                          backward=True, logits_kind="hot_set"),
+    "v3_select_bias": Workload("v3_select_bias", T=131072, E=256, k=8, capacity_factor=1.25,
+                               alpha=0.0, renorm=True, logits_kind="normal",
+                               select_bias_scale=0.5, bias_gamma=0.001),
 }
 
 
@@ -91,7 +100,8 @@ def make_inputs(w: Workload, seed: int):
     """Draw the inputs of workload ``w`` for ``seed``.
 
     Returns a dict with ``logits`` (float32 [T,E]) or, for the gate workload,
-    ``X`` (uint16 bf16 bits [T,d]) and ``Wg`` (uint16 bf16 bits [d,E]).
+    ``X`` (uint16 bf16 bits [T,d]) and ``Wg`` (uint16 bf16 bits [d,E]); plus
+    ``select_bias`` (float32 [E]) for workloads routed with a selection bias.
     """
     rng = np.random.default_rng(seed)
     if w.d > 0:
@@ -116,4 +126,8 @@ def make_inputs(w: Workload, seed: int):
             L[mb * Tm:(mb + 1) * Tm, h] += np.float32(2.0)
     else:
         raise ValueError(w.logits_kind)
-    return {"logits": np.ascontiguousarray(L, dtype=np.float32)}
+    out = {"logits": np.ascontiguousarray(L, dtype=np.float32)}
+    if w.select_bias_scale > 0:
+        out["select_bias"] = (np.float32(w.select_bias_scale)
+                              * rng.standard_normal(w.E, dtype=np.float32)).astype(np.float32)
+    return out

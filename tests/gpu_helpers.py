@@ -14,7 +14,7 @@ INT_KEYS = ("topk_idx", "counts", "offsets", "perm", "dropped")
 def params_of(w, **over):
     kw = dict(T=w.T, E=w.E, k=w.k, n_micro=w.n_micro, d=w.d,
               capacity_factor=w.capacity_factor, alpha=w.alpha, renorm=w.renorm,
-              save_row_stats=True, inv_perm=True)
+              save_row_stats=True, inv_perm=True, select_bias=w.select_bias_scale > 0)
     kw.update(over)
     return lbs.make_params(**kw)
 
@@ -28,13 +28,15 @@ def gpu_forward(params, inputs, out_extra=None):
             t.fill_(float("nan") if t.is_floating_point() else (0xEE if t.dtype == torch.uint8 else -7))
     ws = lbs.alloc_workspace(params, device=dev)
     ws.fill_(0xAB)
+    sb = inputs.get("select_bias")
+    sb = None if sb is None else torch.from_numpy(np.asarray(sb, np.float32)).to(dev)
     if "logits" in inputs:
         L = torch.from_numpy(inputs["logits"]).to(dev)
-        lbs.moe_route(params, out, ws, logits=L)
+        lbs.moe_route(params, out, ws, logits=L, select_bias=sb)
     else:
         X = torch.from_numpy(inputs["X"].view(np.int16)).to(dev)
         W = torch.from_numpy(inputs["Wg"].view(np.int16)).to(dev)
-        lbs.moe_route(params, out, ws, X=X, Wg=W)
+        lbs.moe_route(params, out, ws, X=X, Wg=W, select_bias=sb)
     torch.cuda.synchronize()
     res = {k: (None if v is None else v.cpu().numpy()) for k, v in out.items()}
     res["_torch_out"] = out
@@ -54,11 +56,12 @@ def gpu_backward(params, logits, counts, row_stats=None, d_aux=None):
     return dl.cpu().numpy()
 
 
-def oracle_forward(params, logits):
+def oracle_forward(params, logits, select_bias=None):
     cap = params.capacity
     return oracle.route(logits, params.k, n_micro=params.n_micro,
                         capacity_factor=params.capacity_factor, capacity_override=cap,
-                        alpha=params.alpha, renorm=bool(params.flags & lbs.MOE_RENORM_TOPK))
+                        alpha=params.alpha, renorm=bool(params.flags & lbs.MOE_RENORM_TOPK),
+                        select_bias=select_bias)
 
 
 def assert_close_rel(got, ref, rtol, atol=0.0, what=""):

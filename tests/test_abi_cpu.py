@@ -31,8 +31,8 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(lbs):
     lib = lbs.load()
     names = declared_functions()
-    assert set(names) == {"moe_route", "moe_route_backward", "moe_route_capacity",
-                          "moe_route_strerror", "moe_route_workspace_size"}
+    assert set(names) == {"moe_route", "moe_route_backward", "moe_route_bias_update",
+                          "moe_route_capacity", "moe_route_strerror", "moe_route_workspace_size"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", lbs._binding.LIB_PATH],
@@ -107,9 +107,9 @@ def test_moe_route_validates_before_launching(lbs):
     full = {n: fake for n in B._OUT_FIELDS}
     full["logits"] = None
 
-    def call(out_fields, logits=fake, ws=fake, ws_bytes=1 << 20, params=p):
+    def call(out_fields, logits=fake, ws=fake, ws_bytes=1 << 20, params=p, bias=None):
         o = B.moe_route_out(*[out_fields.get(n) for n in B._OUT_FIELDS])
-        return lib.moe_route(ctypes.byref(params), logits, None, None, ctypes.byref(o),
+        return lib.moe_route(ctypes.byref(params), logits, None, None, bias, ctypes.byref(o),
                              ws, ws_bytes, None)
 
     for missing in ["topk_idx", "topk_w", "counts", "offsets", "perm", "dropped", "aux_loss",
@@ -128,7 +128,18 @@ def test_moe_route_validates_before_launching(lbs):
     assert call(f, params=pi) == B.MOE_ERR_INVALID_ARG
     pg = lbs.make_params(64, 8, 2, d=64)
     assert call(full, params=pg) == B.MOE_ERR_INVALID_ARG        # gate path without X/Wg
-    assert lib.moe_route(None, None, None, None, None, None, 0, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(None, None, None, None, None, None, None, 0, None) == B.MOE_ERR_INVALID_ARG
+    # selection bias: required with the flag, must be 4-byte aligned
+    pb = lbs.make_params(64, 8, 2, select_bias=True)
+    assert call(full, params=pb) == B.MOE_ERR_INVALID_ARG
+    assert call(full, params=pb, bias=fake + 2) == B.MOE_ERR_INVALID_ARG
+    # bias update
+    assert lib.moe_route_bias_update(ctypes.byref(p), None, 0.1, fake, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_bias_update(ctypes.byref(p), fake, 0.1, None, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_bias_update(ctypes.byref(p), fake, -0.1, fake, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_bias_update(ctypes.byref(p), fake, float("nan"), fake, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_bias_update(ctypes.byref(lbs.make_params(0, 8, 1)), fake, 0.1, fake,
+                                     None) == B.MOE_ERR_INVALID_ARG
     # backward
     assert lib.moe_route_backward(ctypes.byref(p), None, None, fake, None, fake, None) \
         == B.MOE_ERR_INVALID_ARG
