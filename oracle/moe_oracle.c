@@ -75,6 +75,33 @@ void oracle_gate_logits(const uint16_t *X, const uint16_t *Wg, long long T,
         }
 }
 
+/*
+ * Backward of the gate GEMM logits = X.Wg (bf16 inputs, see above):
+ *   dX[t][i]  = sum_e dlogits[t][e] * Wg[i][e]      (dX  = dlogits . Wg^T)
+ *   dWg[i][e] = sum_t X[t][i] * dlogits[t][e]       (dWg = X^T . dlogits)
+ * in double; either output may be NULL.
+ */
+void oracle_gate_backward(const uint16_t *X, const uint16_t *Wg, const double *dlogits,
+                          long long T, long long d, long long E, double *dX, double *dWg)
+{
+    if (dX)
+        for (long long t = 0; t < T; ++t)
+            for (long long i = 0; i < d; ++i) {
+                double acc = 0.0;
+                for (long long e = 0; e < E; ++e)
+                    acc += dlogits[t * E + e] * bf16_to_double(Wg[i * E + e]);
+                dX[t * d + i] = acc;
+            }
+    if (dWg)
+        for (long long i = 0; i < d; ++i)
+            for (long long e = 0; e < E; ++e) {
+                double acc = 0.0;
+                for (long long t = 0; t < T; ++t)
+                    acc += bf16_to_double(X[t * d + i]) * dlogits[t * E + e];
+                dWg[i * E + e] = acc;
+            }
+}
+
 /* Row softmax statistics: m = max_e l, s = sum_e exp(l - m). */
 static void softmax_stats(const double *row, long long E, double *m_out, double *s_out)
 {
@@ -123,6 +150,12 @@ static void topk_row(const double *row, long long E, long long k, int32_t *idx, 
  * aux loss keep the unbiased softmax -- and the biased value is the fp32 sum
  * l + b_i (the precision the logits and the bias are given in).
  *
+ * p_masked: P_i from the picked positions only, as [p1] 4.4 codes it: the
+ * softmax is zeroed outside each token's k picks and the sum is divided by
+ * the number of assignments Tm*k (for k = 1 this is [p2] 3.1's masked mean
+ * over tokens).  Otherwise P_i is the mean softmax over all tokens ([p1]
+ * 4.2).  The picks are the pre-capacity top-k.
+ *
  * Outputs (all caller-allocated; pointers marked "may be NULL" are skipped):
  *   topk_idx [T*k], topk_w [T*k]          selection and gate weights
  *   row_max, row_sum [T]      (may be NULL) softmax statistics
@@ -140,7 +173,7 @@ static void topk_row(const double *row, long long E, long long k, int32_t *idx, 
  */
 int oracle_route(const double *logits, long long T, long long E, long long k,
                  long long n_micro, long long capacity, double alpha, int renorm,
-                 const float *select_bias, int32_t *topk_idx, double *topk_w, double *row_max, double *row_sum,
+                 const float *select_bias, int p_masked, int32_t *topk_idx, double *topk_w, double *row_max, double *row_sum,
                  int32_t *counts, int32_t *offsets, int32_t *perm, int32_t *inv_perm,
                  uint8_t *dropped, double *f, double *P, double *aux, double *cv,
                  double *max_over_mean, double *extra)
@@ -176,8 +209,9 @@ int oracle_route(const double *logits, long long T, long long E, long long k,
             softmax_stats(row, E, &m, &s);
             if (row_max) row_max[t] = m;
             if (row_sum) row_sum[t] = s;
-            for (long long e = 0; e < E; ++e)
-                psum[e] += exp(row[e] - m) / s;
+            if (!p_masked)
+                for (long long e = 0; e < E; ++e)
+                    psum[e] += exp(row[e] - m) / s;
 
             int32_t *idx = topk_idx + t * k;
             if (select_bias) {
@@ -198,6 +232,8 @@ int oracle_route(const double *logits, long long T, long long E, long long k,
                  * rescaled to sum to one; without it the gate is p itself. */
                 topk_w[t * k + j] = renorm ? p / picked : p;
                 cnt[idx[j]] += 1;
+                if (p_masked)
+                    psum[idx[j]] += p;
             }
         }
 
@@ -236,7 +272,7 @@ int oracle_route(const double *logits, long long T, long long E, long long k,
         long long kept = 0;
         for (long long e = 0; e < E; ++e) {
             double fe = (double)cnt[e] / total;
-            double pe = psum[e] / (double)Tm;
+            double pe = psum[e] / (p_masked ? total : (double)Tm);
             f[mb * E + e] = fe;
             P[mb * E + e] = pe;
             dot += fe * pe;
@@ -294,34 +330,76 @@ void oracle_bias_update(const int32_t *counts, long long n_micro, long long E,
 }
 
 /*
- * Gradient of the aux loss with respect to the logits.
- * [p1] 4.2 and [p2] 2.2: f_i is a hard observation with no gradient; the
- * gradient flows through P_i only.  With P_i = (1/Tm) sum_t p[t][i] and
- * dp[t][i]/dl[t][j] = p[t][i] (delta_ij - p[t][j]):
- *   dL/dl[t][j] = g * alpha * E / Tm * p[t][j] * (f_j - sum_i f_i p[t][i])
- * where g is the upstream gradient of the microbatch's loss (1 if NULL).
+ * Gradient with respect to the logits of
+ *   L = sum_mb g_mb * aux_mb + sum_{t,j} dW[t][j] * w[t][j]
+ * with the selection (topk_idx) and the counts f held fixed ([p1] 4.2 and
+ * [p2] 2.2: the routing choice and f_i are hard observations; the gradient
+ * reaches the router through the probabilities only).
+ *   aux_mb = alpha * E * sum_i f_i * P_i, P_i = (1/Tm) sum_t p[t][i], or with
+ *   p_masked (([p1] 4.4) P_i = (1/(Tm*k)) sum_t m[t][i] p[t][i], m[t][i] = 1
+ *   when i is one of t's picks;
+ *   w[t][j] = p[t][idx_j], or p[t][idx_j] / sum_j' p[t][idx_j'] with renorm.
+ * Written as the chain rule through the probabilities: for each token the
+ * vector G_i = dL/dp[t][i] is formed from the two terms, then the softmax
+ * Jacobian dp_i/dl_j = p_i (delta_ij - p_j) gives
+ *   dL/dl[t][j] = p_j (G_j - sum_i G_i p_i).
+ * g_mb is d_aux[mb] (1 if NULL); d_topk_w [T*k] may be NULL (no weight term).
  */
 void oracle_backward(const double *logits, long long T, long long E, long long k,
                      long long n_micro, double alpha, const int32_t *counts,
-                     const double *d_aux, double *dlogits)
+                     const double *d_aux, int p_masked, const int32_t *topk_idx,
+                     int renorm, const double *d_topk_w, double *dlogits)
 {
     const long long Tm = T / n_micro;
+    double *p = (double *)malloc(sizeof(double) * (size_t)E);
+    double *G = (double *)malloc(sizeof(double) * (size_t)E);
+    if (!p || !G) {
+        free(p); free(G);
+        return;
+    }
     for (long long mb = 0; mb < n_micro; ++mb) {
         const double g = d_aux ? d_aux[mb] : 1.0;
-        const double c = g * alpha * (double)E / (double)Tm;
         const int32_t *cnt = counts + mb * E;
+        const double total = (double)(Tm * k);
         for (long long t = mb * Tm; t < (mb + 1) * Tm; ++t) {
             const double *row = logits + t * E;
             double m, s;
             softmax_stats(row, E, &m, &s);
-            double dotfp = 0.0;
             for (long long i = 0; i < E; ++i)
-                dotfp += ((double)cnt[i] / (double)(Tm * k)) * (exp(row[i] - m) / s);
-            for (long long j = 0; j < E; ++j) {
-                double p = exp(row[j] - m) / s;
-                double fj = (double)cnt[j] / (double)(Tm * k);
-                dlogits[t * E + j] = c * p * (fj - dotfp);
+                p[i] = exp(row[i] - m) / s;
+            /* aux term: dP_i/dp[t][i] = 1/Tm, or m[t][i]/(Tm*k) when masked */
+            for (long long i = 0; i < E; ++i)
+                G[i] = p_masked ? 0.0 : g * alpha * (double)E * ((double)cnt[i] / total) / (double)Tm;
+            if (p_masked)
+                for (long long j = 0; j < k; ++j) {
+                    long long i = topk_idx[t * k + j];
+                    G[i] += g * alpha * (double)E * ((double)cnt[i] / total) / total;
+                }
+            /* weight term */
+            if (d_topk_w) {
+                double z = 0.0;
+                for (long long j = 0; j < k; ++j)
+                    z += p[topk_idx[t * k + j]];
+                for (long long j = 0; j < k; ++j) {
+                    long long i = topk_idx[t * k + j];
+                    if (!renorm) {
+                        G[i] += d_topk_w[t * k + j]; /* w_j = p_i */
+                    } else {
+                        /* w_j = p_i / z: dw_j/dp_i = 1/z - p_i/z^2 and
+                           dw_j'/dp_i = -p_idx_j'/z^2 for the other picks */
+                        G[i] += d_topk_w[t * k + j] / z;
+                        for (long long j2 = 0; j2 < k; ++j2)
+                            G[i] -= d_topk_w[t * k + j2] * p[topk_idx[t * k + j2]] / (z * z);
+                    }
+                }
             }
+            double gp = 0.0;
+            for (long long i = 0; i < E; ++i)
+                gp += G[i] * p[i];
+            for (long long j = 0; j < E; ++j)
+                dlogits[t * E + j] = p[j] * (G[j] - gp);
         }
     }
+    free(p);
+    free(G);
 }

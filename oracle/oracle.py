@@ -27,10 +27,12 @@ def load_library(path=None):
     lib.oracle_capacity.restype = ll
     lib.oracle_gate_logits.argtypes = [vp, vp, ll, ll, ll, vp]
     lib.oracle_gate_logits.restype = None
-    lib.oracle_route.argtypes = [vp, ll, ll, ll, ll, ll, d, i] + [vp] * 16
+    lib.oracle_route.argtypes = [vp, ll, ll, ll, ll, ll, d, i, vp, i] + [vp] * 15
     lib.oracle_route.restype = i
-    lib.oracle_backward.argtypes = [vp, ll, ll, ll, ll, d, vp, vp, vp]
+    lib.oracle_backward.argtypes = [vp, ll, ll, ll, ll, d, vp, vp, i, vp, i, vp, vp]
     lib.oracle_backward.restype = None
+    lib.oracle_gate_backward.argtypes = [vp, vp, vp, ll, ll, ll, vp, vp]
+    lib.oracle_gate_backward.restype = None
     lib.oracle_bias_update.argtypes = [vp, ll, ll, ll, ll, ctypes.c_float, vp]
     lib.oracle_bias_update.restype = None
     if path is None:
@@ -62,12 +64,28 @@ def gate_logits(X_bits, Wg_bits, lib=None):
     return out
 
 
+def gate_backward(X_bits, Wg_bits, dlogits, lib=None):
+    """(dX [T,d], dWg [d,E]) in float64 for logits = X.Wg, given dL/dlogits [T,E]."""
+    lib = lib or load_library()
+    X = np.ascontiguousarray(X_bits, dtype=np.uint16)
+    W = np.ascontiguousarray(Wg_bits, dtype=np.uint16)
+    T, d = X.shape
+    d2, E = W.shape
+    assert d == d2
+    G = np.ascontiguousarray(dlogits, dtype=np.float64).reshape(T, E)
+    dX = np.empty((T, d), np.float64)
+    dW = np.empty((d, E), np.float64)
+    lib.oracle_gate_backward(_p(X), _p(W), _p(G), T, d, E, _p(dX), _p(dW))
+    return dX, dW
+
+
 def route(logits, k, n_micro=1, capacity_factor=1.0, capacity_override=-1,
-          alpha=0.01, renorm=False, select_bias=None, lib=None):
+          alpha=0.01, renorm=False, select_bias=None, p_masked=False, lib=None):
     """Route ``logits`` [T,E] (any float dtype; widened exactly to float64).
 
     ``select_bias``: optional float32 [E] added to the logits for the expert
     choice only (fp32 sum); weights and statistics stay unbiased.
+    ``p_masked``: P_i over the picked positions, divided by Tm*k.
 
     Returns a dict of numpy arrays named like the C-ABI outputs, plus
     ``capacity`` (int, -1 = unlimited).
@@ -92,6 +110,7 @@ def route(logits, k, n_micro=1, capacity_factor=1.0, capacity_override=-1,
     if b is not None and b.shape != (E,):
         raise ValueError("select_bias must have shape [E]")
     rc = lib.oracle_route(_p(L), T, E, int(k), m, C, float(alpha), int(bool(renorm)), _p(b),
+                          int(bool(p_masked)),
                           *[_p(o[n]) for n in ("topk_idx", "topk_w", "row_max", "row_sum",
                                                "counts", "offsets", "perm", "inv_perm",
                                                "dropped", "f", "P", "aux", "cv",
@@ -102,15 +121,23 @@ def route(logits, k, n_micro=1, capacity_factor=1.0, capacity_override=-1,
     return o
 
 
-def backward(logits, k, counts, n_micro=1, alpha=0.01, d_aux=None, lib=None):
-    """dL_aux/dlogits [T,E] (float64) given the forward's pre-capacity counts."""
+def backward(logits, k, counts, n_micro=1, alpha=0.01, d_aux=None, p_masked=False,
+             topk_idx=None, renorm=False, d_topk_w=None, lib=None):
+    """dL/dlogits [T,E] (float64) of  sum_mb d_aux[mb]*aux_mb + sum d_topk_w*topk_w,
+    with the forward's selection and pre-capacity counts held fixed.
+    ``topk_idx`` [T,k] is needed for ``p_masked`` and for ``d_topk_w``."""
     lib = lib or load_library()
     L = np.ascontiguousarray(logits, dtype=np.float64)
     T, E = L.shape
     cnt = np.ascontiguousarray(counts, dtype=np.int32).reshape(n_micro, E)
     g = None if d_aux is None else np.ascontiguousarray(d_aux, dtype=np.float64).reshape(n_micro)
+    if (p_masked or d_topk_w is not None) and topk_idx is None:
+        raise ValueError("topk_idx is required for p_masked and d_topk_w")
+    idx = None if topk_idx is None else np.ascontiguousarray(topk_idx, dtype=np.int32).reshape(T, k)
+    dw = None if d_topk_w is None else np.ascontiguousarray(d_topk_w, dtype=np.float64).reshape(T, k)
     out = np.empty((T, E), np.float64)
-    lib.oracle_backward(_p(L), T, E, int(k), int(n_micro), float(alpha), _p(cnt), _p(g), _p(out))
+    lib.oracle_backward(_p(L), T, E, int(k), int(n_micro), float(alpha), _p(cnt), _p(g),
+                        int(bool(p_masked)), _p(idx), int(bool(renorm)), _p(dw), _p(out))
     return out
 
 

@@ -368,6 +368,77 @@ def pin_backward_autograd(lib):
     assert np.allclose(z2, 0.0, atol=1e-17)
 
 
+def pin_masked_P_as_printed(lib):
+    """[p1] 4.4's top-k code: probabilities zeroed outside each token's picks,
+    summed over tokens and divided by num_tokens * top_k; aux = N * sum f P
+    (times alpha); for top-1 this is [p2] 3.1's masked mean over tokens.
+    Transcribed with torch (float64) and the oracle's own picks."""
+    import torch
+    rng = np.random.default_rng(24)
+    for E, k, m, alpha in [(10, 3, 1, 0.1), (16, 1, 2, 0.01), (7, 7, 1, 1.0)]:
+        Tm = 50
+        L = rng.standard_normal((Tm * m, E)).astype(np.float32)
+        o = _route(lib, L, k, n_micro=m, capacity_factor=0.0, alpha=alpha, p_masked=True)
+        probs = torch.softmax(torch.from_numpy(L.astype(np.float64)), dim=-1)
+        for mb in range(m):
+            pr = probs[mb * Tm:(mb + 1) * Tm]
+            idx = torch.from_numpy(o["topk_idx"][mb * Tm:(mb + 1) * Tm].astype(np.int64))
+            mask = torch.zeros_like(pr)
+            for j in range(k):
+                mask.scatter_(1, idx[:, j:j + 1], 1.0)
+            P = ((pr * mask).sum(dim=0) / (Tm * k)).numpy()
+            assert np.allclose(o["P"][mb], P, rtol=1e-13, atol=1e-16)
+            f = np.bincount(idx.numpy().ravel(), minlength=E) / (Tm * k)
+            assert abs(o["aux"][mb] - alpha * E * float(np.dot(f, P))) < 1e-13
+            if k == 1:  # [p2] 3.1: divide by the number of tokens
+                P2 = (pr * torch.nn.functional.one_hot(idx[:, 0], E)).sum(0) / Tm
+                assert np.allclose(o["P"][mb], P2.numpy(), rtol=1e-13, atol=1e-16)
+        if k == E:  # every expert picked by every token: masked P = mean P / k
+            o2 = _route(lib, L, k, capacity_factor=0.0, alpha=alpha)
+            assert np.allclose(o["P"], o2["P"] / k, rtol=1e-13)
+
+
+def pin_backward_full_autograd(lib):
+    """torch.autograd (float64) of  sum_mb g_mb * aux_mb + sum dW * topk_w  with
+    the selection and f detached, for all-token and masked P, with and
+    without renormalised weights, with and without the weight term."""
+    import torch
+    rng = np.random.default_rng(25)
+    E, k, m, Tm, alpha = 9, 3, 2, 15, 0.2
+    L = rng.standard_normal((Tm * m, E))
+    g = np.array([0.7, -1.3])
+    dW = rng.standard_normal((Tm * m, k))
+    for masked in (False, True):
+        for renorm in (False, True):
+            for with_w in (False, True):
+                o = _route(lib, L, k, n_micro=m, capacity_factor=0.0, alpha=alpha,
+                           renorm=renorm, p_masked=masked)
+                got = oracle.backward(L, k, o["counts"], n_micro=m, alpha=alpha, d_aux=g,
+                                      p_masked=masked, topk_idx=o["topk_idx"], renorm=renorm,
+                                      d_topk_w=dW if with_w else None, lib=lib)
+                Lt = torch.tensor(L, requires_grad=True)
+                p = torch.softmax(Lt, dim=-1)
+                idx = torch.from_numpy(o["topk_idx"].astype(np.int64))
+                f = torch.tensor(o["counts"] / (Tm * k))
+                pr = p.reshape(m, Tm, E)
+                if masked:
+                    mask = torch.zeros(Tm * m, E, dtype=torch.float64)
+                    mask.scatter_(1, idx, 1.0)
+                    P = (pr * mask.reshape(m, Tm, E)).sum(dim=1) / (Tm * k)
+                else:
+                    P = pr.mean(dim=1)
+                loss = (torch.tensor(g) * alpha * E * (f * P).sum(dim=1)).sum()
+                if with_w:
+                    w = torch.gather(p, 1, idx)
+                    if renorm:
+                        w = w / w.sum(dim=1, keepdim=True)
+                    assert np.allclose(w.detach().numpy(), o["topk_w"], rtol=1e-13)
+                    loss = loss + (torch.tensor(dW) * w).sum()
+                loss.backward()
+                assert np.allclose(got, Lt.grad.numpy(), rtol=1e-11, atol=1e-14), (masked, renorm, with_w)
+                assert np.allclose(got.sum(axis=1), 0.0, atol=1e-13)
+
+
 # ---------------------------------------------------------------- gate GEMM
 def pin_gate_logits_vs_matmul(lib):
     """The gate logits equal torch.matmul in float64 of the widened bf16
@@ -463,6 +534,26 @@ def pin_bias_update_rule(lib):
     want = np.where(load * E > T * k, b0 - g, np.where(load * E < T * k, b0 + g, b0)).astype(np.float32)
     got = oracle.bias_update(cnt, T=T, k=k, gamma=float(g), bias=b0, lib=lib)
     assert np.array_equal(got, want)
+
+
+
+
+def pin_gate_backward_autograd(lib):
+    """dX and dWg of logits = X.Wg equal torch.autograd (float64) of
+    sum(dlogits * (X.Wg)) over the widened bf16 inputs."""
+    import torch
+    from load_balancing_statistics_amd.workloads import f32_to_bf16_bits, bf16_bits_to_f32
+    rng = np.random.default_rng(26)
+    T, d, E = 29, 72, 6
+    X = f32_to_bf16_bits(rng.standard_normal((T, d), dtype=np.float32))
+    W = f32_to_bf16_bits(0.02 * rng.standard_normal((d, E), dtype=np.float32))
+    G = rng.standard_normal((T, E))
+    dX, dW = oracle.gate_backward(X, W, G, lib=lib)
+    Xt = torch.tensor(bf16_bits_to_f32(X).astype(np.float64), requires_grad=True)
+    Wt = torch.tensor(bf16_bits_to_f32(W).astype(np.float64), requires_grad=True)
+    (torch.tensor(G) * (Xt @ Wt)).sum().backward()
+    assert np.allclose(dX, Xt.grad.numpy(), rtol=1e-13, atol=1e-16)
+    assert np.allclose(dW, Wt.grad.numpy(), rtol=1e-13, atol=1e-16)
 
 
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

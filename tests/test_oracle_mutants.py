@@ -43,17 +43,31 @@ MUTANTS = {
     "cv_sample_std": ("var /= (double)E;", "var /= (double)(E - 1);"),
     "renorm_ignored": ("topk_w[t * k + j] = renorm ? p / picked : p;",
                        "topk_w[t * k + j] = p;"),
-    "grad_sign": ("dlogits[t * E + j] = c * p * (fj - dotfp);",
-                  "dlogits[t * E + j] = c * p * (dotfp - fj);"),
-    "grad_missing_p": ("dlogits[t * E + j] = c * p * (fj - dotfp);",
-                       "dlogits[t * E + j] = c * (fj - dotfp);"),
-    "grad_missing_E": ("const double c = g * alpha * (double)E / (double)Tm;",
-                       "const double c = g * alpha / (double)Tm;"),
-    "gate_transposed_Wg": ("bf16_to_double(Wg[i * E + e])",
-                           "bf16_to_double(Wg[(e * d + i) % (d * E)])"),
+    "grad_sign": ("dlogits[t * E + j] = p[j] * (G[j] - gp);",
+                  "dlogits[t * E + j] = p[j] * (gp - G[j]);"),
+    "grad_missing_p": ("dlogits[t * E + j] = p[j] * (G[j] - gp);",
+                       "dlogits[t * E + j] = (G[j] - gp);"),
+    "grad_missing_E": ("G[i] = p_masked ? 0.0 : g * alpha * (double)E * ((double)cnt[i] / total) / (double)Tm;",
+                       "G[i] = p_masked ? 0.0 : g * alpha * ((double)cnt[i] / total) / (double)Tm;"),
+    "grad_masked_over_Tm": ("G[i] += g * alpha * (double)E * ((double)cnt[i] / total) / total;",
+                            "G[i] += g * alpha * (double)E * ((double)cnt[i] / total) / (double)Tm;"),
+    "grad_renorm_no_cross_term": ("G[i] -= d_topk_w[t * k + j2] * p[topk_idx[t * k + j2]] / (z * z);",
+                                  "G[i] -= 0.0 * z;"),
+    "grad_weight_term_ignored": ("G[i] += d_topk_w[t * k + j]; /* w_j = p_i */",
+                                 "G[i] += 0.0; /* w_j = p_i */"),
+    "masked_P_over_Tm": ("double pe = psum[e] / (p_masked ? total : (double)Tm);",
+                         "double pe = psum[e] / (double)Tm;"),
+    "masked_P_all_tokens": ("            if (!p_masked)\n                for (long long e = 0; e < E; ++e)",
+                            "            if (1)\n                for (long long e = 0; e < E; ++e)"),
+    "gate_transposed_Wg": ("acc += bf16_to_double(X[t * d + i]) * bf16_to_double(Wg[i * E + e]);",
+                           "acc += bf16_to_double(X[t * d + i]) * bf16_to_double(Wg[(e * d + i) % (d * E)]);"),
     "entropy_log2": ("ent -= fe * log(fe);", "ent -= fe * log2(fe);"),
     "balance_degree_sign": ("x[1] = 1.0 - (cmax - mean) / mean;",
                             "x[1] = 1.0 + (cmax - mean) / mean;"),
+    "gate_dX_transposed_Wg": ("acc += dlogits[t * E + e] * bf16_to_double(Wg[i * E + e]);",
+                              "acc += dlogits[t * E + e] * bf16_to_double(Wg[(e * d + i) % (d * E)]);"),
+    "gate_dWg_wrong_row": ("acc += bf16_to_double(X[t * d + i]) * dlogits[t * E + e];",
+                           "acc += bf16_to_double(X[t * d + (i + 1) % d]) * dlogits[t * E + e];"),
     "bias_ignored": ("topk_row(selrow, E, k, idx, taken);",
                      "topk_row(row, E, k, idx, taken);"),
     "bias_added_in_double": ("selrow[e] = (double)biased;",
