@@ -553,7 +553,7 @@ def pin_gate_backward_autograd(lib):
     Wt = torch.tensor(bf16_bits_to_f32(W).astype(np.float64), requires_grad=True)
     (torch.tensor(G) * (Xt @ Wt)).sum().backward()
     assert np.allclose(dX, Xt.grad.numpy(), rtol=1e-13, atol=1e-16)
-    assert np.allclose(dW, Wt.grad.numpy(), rtol=1e-13, atol=1e-16)
+    assert np.allclose(dW, Wt.grad.numpy(), rtol=1e-12, atol=1e-13)  # sums of 29 terms
 
 
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]
