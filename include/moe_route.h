@@ -55,6 +55,9 @@ extern "C" {
 #define MOE_SAVE_ROW_STATS 2u /* write per-token softmax (max, sum)         */
 #define MOE_WRITE_INV_PERM 4u /* write inv_perm                             */
 #define MOE_SELECT_BIAS    8u /* moe_route's select_bias [E] steers the choice */
+#define MOE_P_MASKED      16u /* P_e from each token's picks only, over Tm*k
+                                 ([p1] 4.4's top-k code); default: the mean
+                                 softmax over all tokens ([p1] 4.2)          */
 
 /* Bits of the optional status word (set for the whole call). */
 #define MOE_STATUS_NONFINITE 1 /* a row had a NaN/+inf logit, or only -inf;
@@ -93,7 +96,9 @@ typedef struct {
  *   dropped  [T*k] uint8   1 when the assignment is the (C+1)-th or later of
  *                          its expert in its microbatch ([p1] 4.5)
  *   f, P     [m,E] fp32    nullable; f_e = counts/(Tm*k); P_e = mean over
- *                          the microbatch's tokens of softmax_e ([p1] 4.2)
+ *                          the microbatch's tokens of softmax_e ([p1] 4.2),
+ *                          or with MOE_P_MASKED the sum of softmax_e over the
+ *                          tokens that picked e, divided by Tm*k ([p1] 4.4)
  *   aux_loss [m] fp32      alpha * E * sum_e f_e * P_e ([p2] 2.2)
  *   cv       [m] fp32      population std / mean of counts ([p3] 3.1)
  *   max_over_mean [m] fp32 max(counts) / mean ([p1] 5.4)
@@ -175,18 +180,29 @@ int moe_route_bias_update(const moe_route_params *p, const int32_t *counts, floa
                           float *bias, void *stream);
 
 /*
- * Gradient of the aux loss with respect to the logits ([p1] 4.2: f carries
- * no gradient, P does; [p2] 2.2):
- *   dlogits[t,j] = g_mb * alpha * E / Tm * p[t,j] * (f_j - sum_i f_i p[t,i])
+ * Gradient with respect to the logits of
+ *   L = sum_mb g_mb * aux_mb + sum_{t,j} d_topk_w[t,j] * topk_w[t,j]
+ * with the forward's selection and counts held fixed ([p1] 4.2, [p2] 2.2:
+ * f and the choice carry no gradient, the probabilities do):
+ *   aux, all-token P:  dlogits[t,j] = g alpha E / Tm * p_j (f_j - sum_i f_i p_i)
+ *   aux, MOE_P_MASKED ([p1] 4.4):  g alpha E / (Tm k) * p_j (f_j m_j -
+ *                      sum_i f_i m_i p_i), m_i = 1 for t's picks
+ *   gate weights:      the softmax Jacobian applied to d_topk_w; with
+ *                      MOE_RENORM_TOPK through the renormalisation too
+ *                      (then only the picked logits receive a gradient).
  * logits [T,E] fp32 (for the gate path: the logits moe_route wrote);
  * row_stats [T,2] nullable (the forward's MOE_SAVE_ROW_STATS output; NULL
  * recomputes them); counts [m,E] the forward's counts; d_aux [m] nullable
- * upstream gradient of each microbatch's aux loss (NULL = 1); dlogits
- * [T,E] fp32 output.  p->capacity_factor, capacity and flags are ignored.
+ * upstream gradient of each microbatch's aux loss (NULL = 1); topk_idx
+ * [T,k] the forward's picks, required with MOE_P_MASKED or d_topk_w,
+ * otherwise ignored; d_topk_w [T,k] nullable upstream gradient of the gate
+ * weights (NULL = no weight term); dlogits [T,E] fp32 output.
+ * Flags used: MOE_P_MASKED, MOE_RENORM_TOPK; capacity fields are ignored.
  */
 int moe_route_backward(const moe_route_params *p, const float *logits,
                        const float *row_stats, const int32_t *counts,
-                       const float *d_aux, float *dlogits, void *stream);
+                       const float *d_aux, const int32_t *topk_idx,
+                       const float *d_topk_w, float *dlogits, void *stream);
 
 /* Static message for a return code. */
 const char *moe_route_strerror(int code);

@@ -21,6 +21,7 @@ MOE_RENORM_TOPK = 1
 MOE_SAVE_ROW_STATS = 2
 MOE_WRITE_INV_PERM = 4
 MOE_SELECT_BIAS = 8
+MOE_P_MASKED = 16
 
 MOE_STATUS_NONFINITE = 1
 MOE_STATUS_INTERNAL = 2
@@ -79,7 +80,7 @@ def load(path=None):
     lib.moe_route_capacity.restype = ctypes.c_int
     lib.moe_route.argtypes = [P, vp, vp, vp, vp, ctypes.POINTER(moe_route_out), vp, ctypes.c_size_t, vp]
     lib.moe_route.restype = ctypes.c_int
-    lib.moe_route_backward.argtypes = [P, vp, vp, vp, vp, vp, vp]
+    lib.moe_route_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_route_backward.restype = ctypes.c_int
     lib.moe_route_bias_update.argtypes = [P, vp, ctypes.c_float, vp, vp]
     lib.moe_route_bias_update.restype = ctypes.c_int
@@ -91,9 +92,11 @@ def load(path=None):
 
 
 def make_params(T, E, k, n_micro=1, d=0, capacity_factor=1.0, capacity=-1, alpha=0.01,
-                renorm=False, save_row_stats=False, inv_perm=False, select_bias=False):
+                renorm=False, save_row_stats=False, inv_perm=False, select_bias=False,
+                p_masked=False):
     flags = ((MOE_RENORM_TOPK if renorm else 0) | (MOE_SAVE_ROW_STATS if save_row_stats else 0)
-             | (MOE_WRITE_INV_PERM if inv_perm else 0) | (MOE_SELECT_BIAS if select_bias else 0))
+             | (MOE_WRITE_INV_PERM if inv_perm else 0) | (MOE_SELECT_BIAS if select_bias else 0)
+             | (MOE_P_MASKED if p_masked else 0))
     return moe_route_params(int(T), int(E), int(k), int(n_micro), int(d), float(capacity_factor),
                             int(capacity), float(alpha), flags)
 
@@ -150,10 +153,13 @@ def moe_route(params, out, workspace, logits=None, X=None, Wg=None, stream=None,
         raise MoeRouteError(rc, "moe_route")
 
 
-def moe_route_backward(params, logits, counts, dlogits, row_stats=None, d_aux=None, stream=None):
-    """Aux-loss gradient with respect to the logits, written into ``dlogits``."""
+def moe_route_backward(params, logits, counts, dlogits, row_stats=None, d_aux=None,
+                       topk_idx=None, d_topk_w=None, stream=None):
+    """dL/dlogits of the aux loss (all-token or masked P, per the params' flags)
+    plus, when ``d_topk_w`` is given, of sum d_topk_w * topk_w; into ``dlogits``."""
     rc = load().moe_route_backward(ctypes.byref(params), _ptr(logits), _ptr(row_stats),
-                                   _ptr(counts), _ptr(d_aux), _ptr(dlogits), _stream(stream))
+                                   _ptr(counts), _ptr(d_aux), _ptr(topk_idx), _ptr(d_topk_w),
+                                   _ptr(dlogits), _stream(stream))
     if rc != MOE_OK:
         raise MoeRouteError(rc, "moe_route_backward")
 

@@ -12,7 +12,8 @@ namespace {
 
 using moe::RowCfg;
 
-constexpr uint32_t kKnownFlags = MOE_RENORM_TOPK | MOE_SAVE_ROW_STATS | MOE_WRITE_INV_PERM | MOE_SELECT_BIAS;
+constexpr uint32_t kKnownFlags =
+    MOE_RENORM_TOPK | MOE_SAVE_ROW_STATS | MOE_WRITE_INV_PERM | MOE_SELECT_BIAS | MOE_P_MASKED;
 constexpr size_t kMaxLds = 160 * 1024;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -29,7 +30,8 @@ int check_shape(const moe_route_params* p) {
     if (p->d > 0 && !moe::gate_supported(p->T, p->d, p->E)) return MOE_ERR_UNSUPPORTED;
     const bool bias = (p->flags & MOE_SELECT_BIAS) != 0;
     const RowCfg c = moe::choose_rows(p->T, p->E, p->k, p->n_micro, bias);
-    if (c.G < 0 || moe::rows_lds_bytes(c, p->E, p->k, bias) > kMaxLds) return MOE_ERR_UNSUPPORTED;
+    const bool masked = (p->flags & MOE_P_MASKED) != 0;
+    if (c.G < 0 || moe::rows_lds_bytes(c, p->E, p->k, bias, masked) > kMaxLds) return MOE_ERR_UNSUPPORTED;
     if (moe::scatter_lds_bytes(p->E, p->k) > kMaxLds) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
@@ -149,6 +151,7 @@ int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
     ra.T = p->T; ra.E = p->E; ra.k = p->k; ra.Tm = Tm; ra.R = c.R; ra.bpm = c.bpm;
     ra.renorm = (p->flags & MOE_RENORM_TOPK) ? 1 : 0;
     ra.save_stats = (p->flags & MOE_SAVE_ROW_STATS) ? 1 : 0;
+    ra.p_masked = (p->flags & MOE_P_MASKED) ? 1 : 0;
     ra.qcap = moe::rows_queue_cap(c);
     ra.topk_idx = out->topk_idx; ra.topk_w = out->topk_w; ra.row_stats = out->row_stats;
     ra.cnt_part = ws.cnt_part; ra.P_part = ws.P_part; ra.flag_part = ws.flag_part;
@@ -164,6 +167,7 @@ int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
     sa.cnt_part = ws.cnt_part; sa.P_part = ws.P_part; sa.flag_part = ws.flag_part;
     sa.E = p->E; sa.k = p->k; sa.Tm = Tm; sa.bpm = c.bpm; sa.n_micro = p->n_micro; sa.B = c.B;
     sa.nsplit = c.nsplit; sa.capacity = int(capacity_of(p)); sa.alpha = p->alpha;
+    sa.p_masked = (p->flags & MOE_P_MASKED) ? 1 : 0;
     sa.colprefix = ws.colprefix; sa.split_tot = ws.split_tot; sa.split_P = ws.split_P;
     sa.arrive = ws.arrive; sa.status = out->status;
     sa.counts = out->counts; sa.offsets = out->offsets; sa.f = out->f; sa.P = out->P;
@@ -185,21 +189,28 @@ int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
 }
 
 int moe_route_backward(const moe_route_params* p, const float* logits, const float* row_stats,
-                       const int32_t* counts, const float* d_aux, float* dlogits, void* stream) {
+                       const int32_t* counts, const float* d_aux, const int32_t* topk_idx,
+                       const float* d_topk_w, float* dlogits, void* stream) {
     if (!p) return MOE_ERR_INVALID_ARG;
     moe_route_params q = *p;
     q.d = 0;  // the backward reads logits whatever produced them
     const int rc = check_shape(&q);
     if (rc != MOE_OK) return rc;
     if (!logits || !counts || !dlogits) return MOE_ERR_INVALID_ARG;
-    const void* ptrs[] = {logits, row_stats, counts, d_aux, dlogits};
+    const bool masked = (q.flags & MOE_P_MASKED) != 0;
+    if ((masked || d_topk_w) && !topk_idx) return MOE_ERR_INVALID_ARG;
+    const void* ptrs[] = {logits, row_stats, counts, d_aux, topk_idx, d_topk_w, dlogits};
     for (const void* x : ptrs)
         if (x && !aligned(x, 4)) return MOE_ERR_INVALID_ARG;
     const RowCfg c = moe::choose_rows(q.T, q.E, q.k, q.n_micro);
+    if ((masked || d_topk_w) && moe::backward_lds_bytes(c, q.E) > kMaxLds) return MOE_ERR_UNSUPPORTED;
     moe::BackArgs b{};
     b.logits = logits; b.row_stats = row_stats; b.counts = counts; b.d_aux = d_aux; b.dlogits = dlogits;
+    b.topk_idx = topk_idx; b.d_topk_w = d_topk_w;
     b.T = q.T; b.E = q.E; b.k = q.k; b.Tm = q.T / q.n_micro; b.R = c.R; b.bpm = c.bpm;
     b.alpha = q.alpha;
+    b.p_masked = masked ? 1 : 0;
+    b.renorm = (q.flags & MOE_RENORM_TOPK) ? 1 : 0;
     if (moe::launch_route_backward(c, b, static_cast<hipStream_t>(stream)) != hipSuccess) return MOE_ERR_HIP;
     return MOE_OK;
 }

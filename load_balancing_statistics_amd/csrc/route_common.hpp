@@ -117,9 +117,9 @@ inline int rows_queue_cap(const RowCfg& c) {
     return ((c.R + per_iter - 1) / per_iter) * W;
 }
 
-inline size_t rows_lds_bytes(const RowCfg& c, int E, int k, bool bias = false) {
+inline size_t rows_lds_bytes(const RowCfg& c, int E, int k, bool bias = false, bool masked = false) {
     const int W = 64 / c.S;
-    size_t hist = align_up(size_t(E) * 4, 16) * (bias ? 2 : 1);
+    size_t hist = align_up(size_t(E) * 4, 16) * (bias ? 2 : 1) + (masked ? align_up(size_t(E) * 8, 16) : 0);
     size_t rowbuf = size_t(c.NW) * W * row_stride(c.S, c.G) * 4;
     size_t cand = size_t(c.NW) * W * cand_stride(c.S, c.G) * 8;
     size_t sel = size_t(c.NW) * W * k * 8;
@@ -178,6 +178,7 @@ struct RowsArgs {
     const float* bias;  // [E] selection bias, or nullptr
     int T, E, k, Tm, R, bpm;
     int renorm, save_stats;
+    int p_masked;  // P from the picks only (divided by Tm*k later)
     int qcap;  // per-wave queue entries: row groups of the largest block times rows per group
     int32_t* topk_idx;
     float* topk_w;
@@ -196,6 +197,7 @@ struct ScanArgs {
     int E, k, Tm, bpm, n_micro, B, nsplit;
     int capacity;  // < 0: unlimited
     float alpha;
+    int p_masked;  // P_e = probability sum / (Tm*k) instead of / Tm
     int32_t* colprefix;
     int32_t* split_tot;
     double* split_P;
@@ -231,10 +233,20 @@ struct BackArgs {
     const float* row_stats;
     const int32_t* counts;
     const float* d_aux;
+    const int32_t* topk_idx;  // [T,k]; needed for p_masked and d_topk_w
+    const float* d_topk_w;    // [T,k] upstream gradient of the gate weights, or nullptr
     float* dlogits;
     int T, E, k, Tm, R, bpm;
     float alpha;
+    int p_masked, renorm;
 };
+
+// LDS of the backward's sparse variant: f [E4], then per segment two [E4]
+// row buffers.
+inline size_t backward_lds_bytes(const RowCfg& c, int E) {
+    const size_t E4 = size_t((E + 3) & ~3);
+    return (E4 + size_t(c.NW) * (64 / c.S) * 2 * E4) * 4;
+}
 
 struct BiasArgs {
     const int32_t* counts;  // [m,E]

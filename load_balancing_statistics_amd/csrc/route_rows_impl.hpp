@@ -91,6 +91,13 @@ __device__ __forceinline__ void load_row(float (&x)[G], const float* __restrict_
     }
 }
 
+// A probability of a picked expert as a 2^-32 fixed-point integer: masked
+// probability sums are accumulated with integer LDS atomics, so their value
+// does not depend on the order of the additions.
+__device__ __forceinline__ unsigned long long prob_fixed(float p) {
+    return (p > 0.f) ? (unsigned long long)(double(p) * 4294967296.0 + 0.5) : 0ull;
+}
+
 template <int S, int G, int VEC, bool PAD, int NW, bool BIAS>
 struct RowPass {
     static constexpr int W = 64 / S;               // rows per wave at a time
@@ -134,7 +141,8 @@ struct RowPass {
     __device__ __forceinline__ static void process(
         const RowsArgs& a, const float (&x)[G], long row, bool valid, int s,
         float* rowbuf, uint64_t* cand, int* hist, float (&acc)[G], int& bad,
-        int* queue, int& qn, long row_begin, const float (&bz)[G], const float* blds)
+        int* queue, int& qn, long row_begin, const float (&bz)[G], const float* blds,
+        unsigned long long* pm)
     {
         const int E = a.E, k = a.k;
         // ---- row maximum (softmax) and the candidate threshold tau
@@ -206,8 +214,10 @@ struct RowPass {
         ssum = seg_sum<S>(ssum);
         const float inv = __builtin_amdgcn_rcpf(ssum);
         if (valid) {
+            if (!a.p_masked) {
 #pragma unroll
-            for (int g = 0; g < G; ++g) acc[g] = fmaf(ex[g], inv, acc[g]);
+                for (int g = 0; g < G; ++g) acc[g] = fmaf(ex[g], inv, acc[g]);
+            }
             if (!(ssum > 0.f && ssum <= 3.0e38f)) bad = 1;
         }
 
@@ -284,6 +294,7 @@ struct RowPass {
                     a.topk_idx[row * k + wrank[p]] = wcol[p];
                     a.topk_w[row * k + wrank[p]] = we[p] * rden;
                     atomicAdd(&hist[wcol[p]], 1);
+                    if (a.p_masked) atomicAdd(&pm[wcol[p]], prob_fixed(we[p] * inv));
                 }
             }
             if (s == 0 && a.save_stats) {
@@ -298,7 +309,7 @@ struct RowPass {
     // accumulated by the streaming pass.
     __device__ __forceinline__ static void resolve_queue(
         const RowsArgs& a, const int* queue, int qn, long row_begin, int s, int seg,
-        float* rowbuf, uint64_t* sel, int* hist, const float* blds)
+        float* rowbuf, uint64_t* sel, int* hist, const float* blds, unsigned long long* pm)
     {
         const int E = a.E, k = a.k;
         for (int q0 = 0; q0 < qn; q0 += W) {
@@ -332,6 +343,7 @@ struct RowPass {
                 a.topk_idx[row * k + s] = col;
                 a.topk_w[row * k + s] = e * rden;
                 atomicAdd(&hist[col], 1);
+                if (a.p_masked) atomicAdd(&pm[col], prob_fixed(e * __builtin_amdgcn_rcpf(ssum)));
             }
         }
     }
@@ -348,8 +360,10 @@ route_rows_kernel(const RowsArgs a)
     const int E = a.E, k = a.k;
     int* hist = reinterpret_cast<int*>(smem);
     float* blds = reinterpret_cast<float*>(smem + ((E * 4 + 15) & ~15));  // [E] when BIAS
+    unsigned long long* pm = reinterpret_cast<unsigned long long*>(
+        reinterpret_cast<unsigned char*>(blds) + (BIAS ? ((E * 4 + 15) & ~15) : 0));  // [E] when masked
     float* rowbuf_all = reinterpret_cast<float*>(
-        reinterpret_cast<unsigned char*>(blds) + (BIAS ? ((E * 4 + 15) & ~15) : 0));
+        reinterpret_cast<unsigned char*>(pm) + (a.p_masked ? ((E * 8 + 15) & ~15) : 0));
     uint64_t* cand_all = reinterpret_cast<uint64_t*>(
         reinterpret_cast<unsigned char*>(rowbuf_all) + ((NW * W * RS * 4 + 15) & ~15));
     uint64_t* sel_all = cand_all + NW * W * CS;
@@ -364,6 +378,8 @@ route_rows_kernel(const RowsArgs a)
     for (int e = tid; e < E; e += NW * 64) hist[e] = 0;
     if constexpr (BIAS)
         for (int e = tid; e < E; e += NW * 64) blds[e] = a.bias[e];
+    if (a.p_masked)
+        for (int e = tid; e < E; e += NW * 64) pm[e] = 0ull;
     if (blockIdx.x == 0)
         for (int m = tid; m < a.n_micro; m += NW * 64) a.arrive[m] = 0;
     __syncthreads();
@@ -404,22 +420,22 @@ route_rows_kernel(const RowsArgs a)
     int it = 0;
     for (; it + 2 < iters; it += 2) {
         load_row<S, G, VEC, PAD>(xb, a.logits, clamp(row_at(it + 1)), E, s);
-        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin, bz, blds);
+        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin, bz, blds, pm);
         load_row<S, G, VEC, PAD>(xa, a.logits, clamp(row_at(it + 2)), E, s);
         RP::process(a, xb, row_at(it + 1), row_at(it + 1) < row_end, s, rowbuf, cand, hist,
-                    acc, bad, queue, qn, row_begin, bz, blds);
+                    acc, bad, queue, qn, row_begin, bz, blds, pm);
     }
     if (it + 1 < iters) {
         load_row<S, G, VEC, PAD>(xb, a.logits, clamp(row_at(it + 1)), E, s);
-        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin, bz, blds);
+        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin, bz, blds, pm);
         RP::process(a, xb, row_at(it + 1), row_at(it + 1) < row_end, s, rowbuf, cand, hist,
-                    acc, bad, queue, qn, row_begin, bz, blds);
+                    acc, bad, queue, qn, row_begin, bz, blds, pm);
     } else if (it < iters) {
-        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin, bz, blds);
+        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin, bz, blds, pm);
     }
 
     if (__builtin_expect(qn > 0, 0))
-        RP::resolve_queue(a, queue, qn, row_begin, s, seg, rowbuf, sel, hist, blds);
+        RP::resolve_queue(a, queue, qn, row_begin, s, seg, rowbuf, sel, hist, blds, pm);
 
     // ---- block partials: probability sums (fixed order) and histogram.
     // Lanes with the same s in different segments own the same columns.
@@ -445,20 +461,38 @@ route_rows_kernel(const RowsArgs a)
     const long bo = long(blockIdx.x) * E;
     for (int e = tid; e < E; e += NW * 64) {
         float t = 0.f;
+        if (a.p_masked) {
+            t = float(double(pm[e]) * 0x1p-32);
+        } else {
 #pragma unroll
-        for (int w = 0; w < NW; ++w) t += pbuf[w * E + e];
+            for (int w = 0; w < NW; ++w) t += pbuf[w * E + e];
+        }
         a.P_part[bo + e] = t;
         a.cnt_part[bo + e] = hist[e];
     }
     if (tid == 0) a.flag_part[blockIdx.x] = any_bad ? MOE_STATUS_NONFINITE : 0;
 }
 
-template <int S, int G, int VEC, bool PAD, int NW>
+// Backward.  Dense part (every column):  p_i * (alpha_i - beta_t);
+// sparse part (the k picked columns):     gamma_i.
+//   all-token aux:  alpha_i = c f_i,  beta_t += c sum_e f_e p_e,  c = g alpha E / Tm
+//   masked aux:     gamma_i += c' f_i p_i,  beta_t += c' sum_picked f_e p_e,
+//                   c' = g alpha E / (Tm k)
+//   weights:        gamma_i += p_i dW_j,  beta_t += sum_j dW_j p_{idx_j}
+//   renormalised:   gamma_i += w_j (dW_j - D_t),  D_t = sum_j dW_j w_j
+// (j = the slot that picked column i; the forms follow from the softmax
+// Jacobian p_i (delta_ij - p_j) and, for the renormalised weights
+// w_j = p_{idx_j} / sum_picked p, the quotient rule).  SP enables the sparse
+// part: the segment's probabilities go to an LDS row buffer, the slot lanes
+// (s < k) form the picked columns' terms and write them into a second
+// per-segment buffer, which the column owners read and clear again.
+template <int S, int G, int VEC, bool PAD, int NW, bool SP>
 __global__ void __launch_bounds__(NW * 64)
 route_backward_kernel(const BackArgs a)
 {
     constexpr int W = 64 / S;
-    const int E = a.E;
+    extern __shared__ __align__(16) unsigned char bsmem[];
+    const int E = a.E, k = a.k;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int seg = lane / S, s = lane % S;
@@ -475,6 +509,20 @@ route_backward_kernel(const BackArgs a)
     }
     const float gup = a.d_aux ? a.d_aux[mb] : 1.0f;
     const float c = gup * a.alpha * float(E) / float(a.Tm);
+    const float cm = c / float(k);
+    const bool dense_aux = !(SP && a.p_masked);
+
+    // SP buffers: f of every expert, then per segment [E4] probabilities and
+    // [E4] sparse terms (kept zero between rows)
+    const int E4 = (E + 3) & ~3;
+    float* fl = reinterpret_cast<float*>(bsmem);
+    float* pb = fl + E4 + (wave * W + seg) * 2 * E4;
+    float* gb = pb + E4;
+    if constexpr (SP) {
+        for (int e = tid; e < E; e += NW * 64) fl[e] = float(a.counts[long(mb) * E + e]) * inv_total;
+        for (int e = s; e < E; e += S) gb[e] = 0.f;
+        __syncthreads();
+    }
 
     const long per_iter = long(NW) * W;
     for (long row = row_begin + long(wave) * W + seg; row - seg < row_end; row += per_iter) {
@@ -511,7 +559,64 @@ route_backward_kernel(const BackArgs a)
             ex[g] *= inv;  // p
             dot = fmaf(fcol[g], ex[g], dot);
         }
-        dot = seg_sum<S>(dot);
+        float beta = 0.f;
+        if (dense_aux) beta = c * seg_sum<S>(dot);
+        float gam[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) gam[g] = 0.f;
+        if constexpr (SP) {
+            // owners publish the row's probabilities
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int col = col_of<S, VEC>(g, s);
+                if (!PAD || col < E) pb[col] = ex[g];
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // slot lanes: the picked columns
+            int cs = -1;
+            float ps = 0.f, fs = 0.f, dws = 0.f;
+            if (valid && s < k) {
+                const int e = a.topk_idx[row * k + s];
+                if (e >= 0 && e < E) {
+                    cs = e;
+                    ps = pb[e];
+                    fs = fl[e];
+                    dws = a.d_topk_w ? a.d_topk_w[row * k + s] : 0.f;
+                }
+            }
+            const float Z = seg_sum<S>(ps);
+            const float Sm = seg_sum<S>(fs * ps);
+            const float Dn = seg_sum<S>(dws * ps);
+            if (a.p_masked) beta += cm * Sm;
+            if (a.d_topk_w && !a.renorm) beta += Dn;
+            if (cs >= 0) {
+                float gv = 0.f;
+                if (a.p_masked) gv += cm * fs * ps;
+                if (a.d_topk_w) {
+                    if (a.renorm) {
+                        const float rz = 1.0f / Z;
+                        gv += ps * rz * (dws - Dn * rz);
+                    } else {
+                        gv += ps * dws;
+                    }
+                }
+                gb[cs] = gv;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // owners take their columns' terms and clear them for the next row
+#pragma unroll
+            for (int g = 0; g < G; ++g) {
+                const int col = col_of<S, VEC>(g, s);
+                if (!PAD || col < E) {
+                    gam[g] = gb[col];
+                    gb[col] = 0.f;
+                }
+            }
+        }
         if (valid) {
             float* dst = a.dlogits + row * E;
             if constexpr (VEC == 4) {
@@ -520,10 +625,12 @@ route_backward_kernel(const BackArgs a)
                     const int c0 = 4 * (j * S + s);
                     if (!PAD || c0 < E) {
                         f32x4 v;
-                        v[0] = c * ex[4 * j + 0] * (fcol[4 * j + 0] - dot);
-                        v[1] = c * ex[4 * j + 1] * (fcol[4 * j + 1] - dot);
-                        v[2] = c * ex[4 * j + 2] * (fcol[4 * j + 2] - dot);
-                        v[3] = c * ex[4 * j + 3] * (fcol[4 * j + 3] - dot);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int g = 4 * j + q;
+                            const float al = dense_aux ? c * fcol[g] : 0.f;
+                            v[q] = ex[g] * (al - beta) + gam[g];
+                        }
                         __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(dst + c0));
                     }
                 }
@@ -531,7 +638,8 @@ route_backward_kernel(const BackArgs a)
 #pragma unroll
                 for (int g = 0; g < G; ++g) {
                     const int col = g * S + s;
-                    if (!PAD || col < E) __builtin_nontemporal_store(c * ex[g] * (fcol[g] - dot), dst + col);
+                    const float al = dense_aux ? c * fcol[g] : 0.f;
+                    if (!PAD || col < E) __builtin_nontemporal_store(ex[g] * (al - beta) + gam[g], dst + col);
                 }
             }
         }
@@ -540,7 +648,7 @@ route_backward_kernel(const BackArgs a)
 
 template <int S, int G, int VEC, bool PAD, int NW, bool BIAS>
 hipError_t launch_rows_nw(const RowCfg& c, const RowsArgs& a, hipStream_t st) {
-    const size_t lds = rows_lds_bytes(c, a.E, a.k, BIAS);
+    const size_t lds = rows_lds_bytes(c, a.E, a.k, BIAS, a.p_masked != 0);
     auto kern = route_rows_kernel<S, G, VEC, PAD, NW, BIAS>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -563,13 +671,27 @@ hipError_t launch_rows(const RowCfg& c, const RowsArgs& a, hipStream_t st) {
     return hipErrorInvalidValue;
 }
 
+template <int S, int G, int VEC, bool PAD, int NW, bool SP>
+hipError_t launch_backward_nw(const RowCfg& c, const BackArgs& a, hipStream_t st) {
+    auto kern = route_backward_kernel<S, G, VEC, PAD, NW, SP>;
+    const size_t lds = SP ? backward_lds_bytes(c, a.E) : 0;
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3(c.B), dim3(NW * 64), lds, st, a);
+    return hipGetLastError();
+}
+
 template <int S, int G, int VEC, bool PAD>
 hipError_t launch_backward(const RowCfg& c, const BackArgs& a, hipStream_t st) {
+    const bool sp = a.p_masked || a.d_topk_w;
     if (c.NW == 16)
-        hipLaunchKernelGGL((route_backward_kernel<S, G, VEC, PAD, 16>), dim3(c.B), dim3(16 * 64), 0, st, a);
-    else
-        hipLaunchKernelGGL((route_backward_kernel<S, G, VEC, PAD, 12>), dim3(c.B), dim3(12 * 64), 0, st, a);
-    return hipGetLastError();
+        return sp ? launch_backward_nw<S, G, VEC, PAD, 16, true>(c, a, st)
+                  : launch_backward_nw<S, G, VEC, PAD, 16, false>(c, a, st);
+    return sp ? launch_backward_nw<S, G, VEC, PAD, 12, true>(c, a, st)
+              : launch_backward_nw<S, G, VEC, PAD, 12, false>(c, a, st);
 }
 
 // Dispatch over (G, VEC, PAD) for one S.

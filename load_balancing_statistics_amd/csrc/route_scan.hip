@@ -14,7 +14,8 @@
 // per microbatch, zeroed by the row pass that precedes this kernel): fp64,
 // every sum in a fixed order:
 //   counts_e, offsets = exclusive prefix sum of the counts,
-//   f_e = counts_e/(Tm*k) and P_e = probability sum/Tm with
+//   f_e = counts_e/(Tm*k) and P_e = probability sum/Tm (or /(Tm*k) for the
+//   masked form of mhpq.cn section 4.4, whose sums cover the picks only) with
 //   aux = alpha*E*sum_e f_e*P_e (mhpq.cn sections 4.2, 4.4; codechina.net
 //   section 2.2), CV = population std/mean and balance degree
 //   1-(max-mean)/mean (page cnvsn.com/news/335486 sections 3.1, 5.1),
@@ -75,7 +76,7 @@ __device__ void microbatch_statistics(const ScanArgs& a, int mb) {
     int cmax = -1, cmin = INT_MAX;
     if (own) {
         const double fe = double(cnt) / total;
-        const double pe = ps / double(a.Tm);
+        const double pe = ps / (a.p_masked ? total : double(a.Tm));
         a.counts[cb + tid] = cnt;
         if (a.f) a.f[cb + tid] = float(fe);
         if (a.P) a.P[cb + tid] = float(pe);

@@ -141,9 +141,12 @@ def test_moe_route_validates_before_launching(lbs):
     assert lib.moe_route_bias_update(ctypes.byref(lbs.make_params(0, 8, 1)), fake, 0.1, fake,
                                      None) == B.MOE_ERR_INVALID_ARG
     # backward
-    assert lib.moe_route_backward(ctypes.byref(p), None, None, fake, None, fake, None) \
-        == B.MOE_ERR_INVALID_ARG
-    assert lib.moe_route_backward(ctypes.byref(p), fake, None, None, None, fake, None) \
-        == B.MOE_ERR_INVALID_ARG
-    assert lib.moe_route_backward(ctypes.byref(p), fake + 1, None, fake, None, fake, None) \
-        == B.MOE_ERR_INVALID_ARG
+    bwd = lib.moe_route_backward
+    assert bwd(ctypes.byref(p), None, None, fake, None, None, None, fake, None) == B.MOE_ERR_INVALID_ARG
+    assert bwd(ctypes.byref(p), fake, None, None, None, None, None, fake, None) == B.MOE_ERR_INVALID_ARG
+    assert bwd(ctypes.byref(p), fake + 1, None, fake, None, None, None, fake, None) == B.MOE_ERR_INVALID_ARG
+    # masked P or a gate-weight gradient need the picks
+    pm = lbs.make_params(64, 8, 2, p_masked=True)
+    assert bwd(ctypes.byref(pm), fake, None, fake, None, None, None, fake, None) == B.MOE_ERR_INVALID_ARG
+    assert bwd(ctypes.byref(p), fake, None, fake, None, None, fake, fake, None) == B.MOE_ERR_INVALID_ARG
+    assert bwd(ctypes.byref(p), fake, None, fake, None, fake + 2, fake, fake, None) == B.MOE_ERR_INVALID_ARG
