@@ -82,12 +82,15 @@ def alg_bytes(w, T):
     gate = (2 * T * d + 2 * d * E + 4 * T * E) if d > 0 else 0
     scatter = 5 * T * k
     bwd = (8 * T * E + 8 * T) if w.backward else 0
+    # gate backward: X read, dX (bf16) written, dlogits and Wg read, dWg written
+    gate_bwd = (4 * T * d + 4 * T * E + 2 * d * E + 4 * d * E) if (d > 0 and w.backward) else 0
     forward = (gate + 8 * T * k + stats + scatter) if d > 0 else (rows + scatter)
     if w.select_bias_scale > 0:
         # selection bias read by the row pass; the update reads the counts
         # and reads and writes the bias
         forward += 4 * E + (4 * w.n_micro * E + 8 * E if w.bias_gamma > 0 else 0)
-    return {"rows": rows, "gate": gate, "scatter": scatter, "backward": bwd, "forward": forward}
+    return {"rows": rows, "gate": gate, "scatter": scatter, "backward": bwd + gate_bwd,
+            "route_backward": bwd, "gate_backward": gate_bwd, "forward": forward}
 
 
 def kernel_source_hash():
@@ -140,7 +143,9 @@ def cpu_baseline(w, inp, budget_s):
         o = oracle.route(lg, w.k, n_micro=m, capacity_factor=w.capacity_factor, alpha=w.alpha,
                          renorm=w.renorm, select_bias=inp.get("select_bias"))
         if w.backward:
-            oracle.backward(lg, w.k, o["counts"], n_micro=m, alpha=w.alpha)
+            dl = oracle.backward(lg, w.k, o["counts"], n_micro=m, alpha=w.alpha)
+            if L is None:
+                oracle.gate_backward(X[:n], Wg, dl)
         if w.bias_gamma > 0:
             oracle.bias_update(o["counts"], T=n, k=w.k, gamma=w.bias_gamma, bias=inp["select_bias"])
         return time.perf_counter() - t0
@@ -157,6 +162,7 @@ def cpu_baseline(w, inp, budget_s):
     sample = (f"oracle (serial C, fp64) on the first {n} tokens of the seed-0 {w.name} inputs"
               f" x{reps} pass(es): forward" + (" + backward" if w.backward else "")
               + (" incl. gate GEMM" if w.d > 0 else "")
+              + (" and its backward" if w.d > 0 and w.backward else "")
               + (" with selection bias" if w.select_bias_scale > 0 else "")
               + (" + bias update" if w.bias_gamma > 0 else ""))
     return {"value": tokens / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
@@ -198,6 +204,12 @@ def main():
     out = lbs.alloc_outputs(p, device=dev)
     ws = lbs.alloc_workspace(p, device=dev)
     dlogits = torch.empty((w.T, w.E), dtype=torch.float32, device=dev) if w.backward else None
+    gate_bwd = w.d > 0 and w.backward
+    if gate_bwd:  # gradients of the gate GEMM's inputs
+        dX = torch.empty((w.T, w.d), dtype=torch.int16, device=dev)
+        dWg = torch.empty((w.d, w.E), dtype=torch.float32, device=dev)
+        ws_gb = torch.empty(max(256, lbs.moe_gate_backward_workspace_size(p)), dtype=torch.uint8,
+                            device=dev)
 
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
@@ -205,6 +217,7 @@ def main():
     K = args.steps
     ev_rows = [(hev.create(), hev.create()) for _ in range(K)]
     ev_bwd = [(hev.create(), hev.create()) for _ in range(K)] if w.backward else None
+    ev_gb = [(hev.create(), hev.create()) for _ in range(K)] if gate_bwd else None
 
     def step(i, timed):
         src = srcs[i % ncopy]
@@ -221,6 +234,12 @@ def main():
                                    stream=stream)
             if timed:
                 hev.record(ev_bwd[i][1], sh)
+        if gate_bwd:
+            if timed:
+                hev.record(ev_gb[i][0], sh)
+            lbs.moe_gate_backward(p, src, Wg, dlogits, dX=dX, dWg=dWg, workspace=ws_gb, stream=stream)
+            if timed:
+                hev.record(ev_gb[i][1], sh)
 
     for i in range(args.warmup):
         step(i, False)
@@ -249,6 +268,7 @@ def main():
     timed_loop(True)
     rows_ms = sum(hev.elapsed_ms(a, b) for a, b in ev_rows) / K
     bwd_ms = sum(hev.elapsed_ms(a, b) for a, b in ev_bwd) / K if w.backward else None
+    gb_ms = sum(hev.elapsed_ms(a, b) for a, b in ev_gb) / K if gate_bwd else None
     status = int(out["status"].item())
 
     # device-to-device copy ceiling (same rotation logic: 1 GiB buffers)
@@ -266,10 +286,12 @@ def main():
     del cbuf, cdst
 
     ab = alg_bytes(w, w.T)
-    if w.d > 0:
+    if gate_bwd:
+        dom_name, dom_bytes, dom_ms = "gate_backward_kernel", ab["gate_backward"], gb_ms
+    elif w.d > 0:
         dom_name, dom_bytes, dom_ms = "gate+route forward (no per-kernel split)", ab["forward"], ms_step
     elif w.backward and bwd_ms > rows_ms:
-        dom_name, dom_bytes, dom_ms = "route_backward_kernel", ab["backward"], bwd_ms
+        dom_name, dom_bytes, dom_ms = "route_backward_kernel", ab["route_backward"], bwd_ms
     else:
         dom_name, dom_bytes, dom_ms = "route_rows_kernel", ab["rows"], rows_ms
     traffic = measured_traffic(w.name, dom_name) if w.d == 0 else None
@@ -306,6 +328,7 @@ def main():
                    "step_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
                    "row_pass_ms": round(rows_ms, 5),
                    "backward_ms": None if bwd_ms is None else round(bwd_ms, 5),
+                   "gate_backward_ms": None if gb_ms is None else round(gb_ms, 5),
                    "copy_ceiling_GBps": round(copy_gbps, 1),
                    "assignments_per_s": w.T * w.k / (ms_step * 1e-3),
                    "input_copies": ncopy, "host_enqueue_s": round(host_s, 4),
@@ -314,8 +337,8 @@ def main():
     print(json.dumps(res), flush=True)
     for a, b in ev_rows:
         hev.destroy(a); hev.destroy(b)
-    if ev_bwd:
-        for a, b in ev_bwd:
+    for evs in (ev_bwd, ev_gb):
+        for a, b in (evs or []):
             hev.destroy(a); hev.destroy(b)
 
 

@@ -204,6 +204,23 @@ int moe_route_backward(const moe_route_params *p, const float *logits,
                        const float *d_aux, const int32_t *topk_idx,
                        const float *d_topk_w, float *dlogits, void *stream);
 
+/*
+ * Backward of the gate GEMM logits = X.Wg (the gate network of [p2] 1.2):
+ *   dX  = dlogits . Wg^T   [T,d] bf16 (fp32 accumulation, rounded to
+ *                          nearest even), nullable
+ *   dWg = X^T . dlogits    [d,E] fp32, nullable (at least one of the two)
+ * Uses p->T, d (> 0) and E (same limits as the gate forward: d % 8 == 0,
+ * E <= 64).  X [T,d] and Wg [d,E] are bf16 bit patterns; X and dX must be
+ * 16-byte aligned.  dlogits [T,E] fp32 is the gradient with respect to the
+ * logits (moe_route_backward's output).  workspace (for dWg only): at least
+ * moe_gate_backward_workspace_size() bytes, 256-byte aligned; scratch.
+ * Deterministic (fixed-order reductions, no atomics).
+ */
+int moe_gate_backward_workspace_size(const moe_route_params *p, size_t *bytes);
+int moe_gate_backward(const moe_route_params *p, const uint16_t *X, const uint16_t *Wg,
+                      const float *dlogits, uint16_t *dX, float *dWg, void *workspace,
+                      size_t workspace_bytes, void *stream);
+
 /* Static message for a return code. */
 const char *moe_route_strerror(int code);
 

@@ -84,6 +84,10 @@ def load(path=None):
     lib.moe_route_backward.restype = ctypes.c_int
     lib.moe_route_bias_update.argtypes = [P, vp, ctypes.c_float, vp, vp]
     lib.moe_route_bias_update.restype = ctypes.c_int
+    lib.moe_gate_backward_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.moe_gate_backward_workspace_size.restype = ctypes.c_int
+    lib.moe_gate_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.moe_gate_backward.restype = ctypes.c_int
     lib.moe_route_strerror.argtypes = [ctypes.c_int]
     lib.moe_route_strerror.restype = ctypes.c_char_p
     if path is None:
@@ -170,6 +174,23 @@ def moe_route_bias_update(params, counts, gamma, bias, stream=None):
                                       _stream(stream))
     if rc != MOE_OK:
         raise MoeRouteError(rc, "moe_route_bias_update")
+
+
+def moe_gate_backward_workspace_size(params):
+    n = ctypes.c_size_t(0)
+    rc = load().moe_gate_backward_workspace_size(ctypes.byref(params), ctypes.byref(n))
+    if rc != MOE_OK:
+        raise MoeRouteError(rc, "moe_gate_backward_workspace_size")
+    return n.value
+
+
+def moe_gate_backward(params, X, Wg, dlogits, dX=None, dWg=None, workspace=None, stream=None):
+    """dX = dlogits.Wg^T (bf16 bits) and/or dWg = X^T.dlogits (fp32) into the given tensors."""
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = load().moe_gate_backward(ctypes.byref(params), _ptr(X), _ptr(Wg), _ptr(dlogits), _ptr(dX),
+                                  _ptr(dWg), _ptr(workspace), nbytes, _stream(stream))
+    if rc != MOE_OK:
+        raise MoeRouteError(rc, "moe_gate_backward")
 
 
 def alloc_outputs(params, device="cuda"):

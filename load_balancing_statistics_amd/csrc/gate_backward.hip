@@ -1,0 +1,206 @@
+// gate_backward.hip -- backward of the gate GEMM logits = X[T,d] . Wg[d,E]:
+//   dX  = dlogits . Wg^T   [T,d]  (bf16, rounded to nearest even)
+//   dWg = X^T . dlogits    [d,E]  (fp32)
+// The gate (router) network of page codechina.net article 413310 section 1.2;
+// dlogits is the routing gradient with respect to the logits.
+//
+// Both products stream X (or dX) once and are bound by HBM (about 6 flop per
+// byte), so they run on the vector ALUs, fused in one pass.  A block owns a
+// 64-column tile of X over a contiguous slice of the tokens; a lane owns CPL
+// consecutive columns of one row per step (CPL = 8, 4, 2, 1 for E <= 8, 16,
+// 32, 64, keeping CPL*E <= 64 fp32 accumulators), so a row's 64 columns are
+// 128 contiguous bytes.  Per row the lane reads its X chunk and the row's E
+// gradients, writes its dX chunk (its CPL x E slice of Wg stays in registers)
+// and adds X * dlogits into its dWg accumulators.  The accumulators are
+// reduced over the lanes and waves of the block in a fixed order into a
+// per-slice partial; a second kernel sums the slices in order.
+// Deterministic: no atomics.
+#include "route_common.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kGbWaves = 4;
+constexpr int kGbThreads = kGbWaves * 64;
+constexpr int kTile = 64;   // columns per block
+constexpr int kRowUnroll = 4;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t((u >> 16) | 0x40u);
+    return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <int CPL>
+__global__ void __launch_bounds__(kGbThreads)
+gate_backward_kernel(const GateBackArgs a)
+{
+    constexpr int EMAX = 64 / CPL;
+    constexpr int LPR = kTile / CPL;       // lanes per row
+    constexpr int RPI = 64 / LPR;          // rows per wave step
+    const int E = a.E, d = a.d;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int cl = lane % LPR, rl = lane / LPR;
+    const int col0 = blockIdx.x * kTile + cl * CPL;
+    const bool col_ok = col0 < d;              // d % 8 == 0 and CPL <= 8: whole chunk in or out
+    const long t0 = (long(blockIdx.y) * a.T) / gridDim.y;
+    const long t1 = (long(blockIdx.y + 1) * a.T) / gridDim.y;
+
+    // the lane's CPL x E slice of Wg
+    float wg[CPL][EMAX];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+        for (int e = 0; e < EMAX; ++e)
+            wg[c][e] = (col_ok && e < E) ? bf16_to_f32(a.Wg[long(col0 + c) * E + e]) : 0.f;
+    float acc[CPL][EMAX];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+        for (int e = 0; e < EMAX; ++e) acc[c][e] = 0.f;
+
+    const long step = long(kGbWaves) * RPI;
+    for (long r0 = t0 + long(wave) * RPI + rl; r0 < t1; r0 += step * kRowUnroll) {
+        uint16_t xv[kRowUnroll][CPL];
+        float gv[kRowUnroll][EMAX];
+#pragma unroll
+        for (int u = 0; u < kRowUnroll; ++u) {
+            const long r = r0 + u * step;
+            const bool in = r < t1;
+            const long rr = in ? r : t0;
+            if constexpr (CPL == 8) {
+                const uint4 v = (col_ok) ? *reinterpret_cast<const uint4*>(a.X + rr * d + col0)
+                                         : make_uint4(0, 0, 0, 0);
+                xv[u][0] = uint16_t(v.x); xv[u][1] = uint16_t(v.x >> 16);
+                xv[u][2] = uint16_t(v.y); xv[u][3] = uint16_t(v.y >> 16);
+                xv[u][4] = uint16_t(v.z); xv[u][5] = uint16_t(v.z >> 16);
+                xv[u][6] = uint16_t(v.w); xv[u][7] = uint16_t(v.w >> 16);
+            } else {
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) xv[u][c] = col_ok ? a.X[rr * d + col0 + c] : uint16_t(0);
+            }
+#pragma unroll
+            for (int e = 0; e < EMAX; ++e) gv[u][e] = (e < E) ? a.dlogits[rr * E + e] : 0.f;
+            if (!in) {
+#pragma unroll
+                for (int e = 0; e < EMAX; ++e) gv[u][e] = 0.f;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kRowUnroll; ++u) {
+            const long r = r0 + u * step;
+            float xf[CPL];
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) xf[c] = bf16_to_f32(xv[u][c]);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+#pragma unroll
+                for (int e = 0; e < EMAX; ++e) acc[c][e] = fmaf(xf[c], gv[u][e], acc[c][e]);
+            if (a.dX && col_ok && r < t1) {
+                uint16_t o[CPL];
+#pragma unroll
+                for (int c = 0; c < CPL; ++c) {
+                    float s = 0.f;
+#pragma unroll
+                    for (int e = 0; e < EMAX; ++e) s = fmaf(gv[u][e], wg[c][e], s);
+                    o[c] = f32_to_bf16(s);
+                }
+                if constexpr (CPL == 8) {
+                    uint4 v;
+                    v.x = uint32_t(o[0]) | (uint32_t(o[1]) << 16);
+                    v.y = uint32_t(o[2]) | (uint32_t(o[3]) << 16);
+                    v.z = uint32_t(o[4]) | (uint32_t(o[5]) << 16);
+                    v.w = uint32_t(o[6]) | (uint32_t(o[7]) << 16);
+                    *reinterpret_cast<uint4*>(a.dX + r * d + col0) = v;
+                } else {
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) a.dX[r * d + col0 + c] = o[c];
+                }
+            }
+        }
+    }
+
+    if (!a.dWg_part) return;
+    // reduce over the lanes that share columns (rows rl of the step): xor
+    // steps LPR, 2*LPR, ... below 64, in a fixed order
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+        for (int e = 0; e < EMAX; ++e) {
+            float v = acc[c][e];
+#pragma unroll
+            for (int m = LPR; m < 64; m <<= 1) v += __shfl_xor(v, m);
+            acc[c][e] = v;
+        }
+    // then over the waves, in wave order, through one LDS tile
+    __shared__ float wred[kTile][EMAX];
+    for (int w = 0; w < kGbWaves; ++w) {
+        if (wave == w && rl == 0) {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c)
+#pragma unroll
+                for (int e = 0; e < EMAX; ++e) {
+                    float& slot = wred[cl * CPL + c][e];
+                    slot = (w == 0) ? acc[c][e] : slot + acc[c][e];
+                }
+        }
+        __syncthreads();
+    }
+    float* part = a.dWg_part + long(blockIdx.y) * d * E;
+    for (int i = threadIdx.x; i < kTile * E; i += kGbThreads) {
+        const int cc = i / E, e = i - (i / E) * E;
+        const int col = blockIdx.x * kTile + cc;
+        if (col < d) part[long(col) * E + e] = wred[cc][e];
+    }
+}
+
+// dWg[i] = sum over the token slices of part[slice][i], slices in order.
+__global__ void __launch_bounds__(256)
+gate_backward_reduce_kernel(const float* __restrict__ part, float* __restrict__ dWg, long n, int slices)
+{
+    for (long i = long(blockIdx.x) * 256 + threadIdx.x; i < n; i += long(gridDim.x) * 256) {
+        float s = 0.f;
+        for (int sl = 0; sl < slices; ++sl) s += part[long(sl) * n + i];
+        dWg[i] = s;
+    }
+}
+
+}  // namespace
+
+// Token slices: enough blocks for two per compute unit, at least 64 rows each.
+int gate_backward_slices(int T, int d) {
+    const long tiles = (d + kTile - 1) / kTile;
+    long sl = (2L * kAssumedCUs + tiles - 1) / tiles;
+    const long max_sl = (T + 63) / 64;
+    if (sl > max_sl) sl = max_sl;
+    if (sl < 1) sl = 1;
+    return int(sl);
+}
+
+size_t gate_backward_workspace_bytes(int T, int d, int E) {
+    return align_up(size_t(gate_backward_slices(T, d)) * d * E * 4, 256);
+}
+
+hipError_t launch_gate_backward(const GateBackArgs& a, hipStream_t st) {
+    const int slices = gate_backward_slices(a.T, a.d);
+    const dim3 grid((a.d + kTile - 1) / kTile, slices);
+    GateBackArgs b = a;
+    if (!a.dWg) b.dWg_part = nullptr;
+    if (a.E <= 8) hipLaunchKernelGGL(gate_backward_kernel<8>, grid, dim3(kGbThreads), 0, st, b);
+    else if (a.E <= 16) hipLaunchKernelGGL(gate_backward_kernel<4>, grid, dim3(kGbThreads), 0, st, b);
+    else if (a.E <= 32) hipLaunchKernelGGL(gate_backward_kernel<2>, grid, dim3(kGbThreads), 0, st, b);
+    else if (a.E <= 64) hipLaunchKernelGGL(gate_backward_kernel<1>, grid, dim3(kGbThreads), 0, st, b);
+    else return hipErrorInvalidValue;
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !a.dWg) return e;
+    const long n = long(a.d) * a.E;
+    const int blocks = int(std::min<long>((n + 255) / 256, 1024));
+    hipLaunchKernelGGL(gate_backward_reduce_kernel, dim3(blocks), dim3(256), 0, st, b.dWg_part, a.dWg, n,
+                       slices);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -230,6 +230,38 @@ int moe_route_bias_update(const moe_route_params* p, const int32_t* counts, floa
     return MOE_OK;
 }
 
+static int check_gate_backward(const moe_route_params* p) {
+    if (!p || p->T < 1 || p->E < 1 || p->d < 1) return MOE_ERR_INVALID_ARG;
+    if (!moe::gate_supported(p->T, p->d, p->E)) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+int moe_gate_backward_workspace_size(const moe_route_params* p, size_t* bytes) {
+    const int rc = check_gate_backward(p);
+    if (rc != MOE_OK) return rc;
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    *bytes = moe::gate_backward_workspace_bytes(p->T, p->d, p->E);
+    return MOE_OK;
+}
+
+int moe_gate_backward(const moe_route_params* p, const uint16_t* X, const uint16_t* Wg,
+                      const float* dlogits, uint16_t* dX, float* dWg, void* workspace,
+                      size_t workspace_bytes_given, void* stream) {
+    const int rc = check_gate_backward(p);
+    if (rc != MOE_OK) return rc;
+    if (!X || !Wg || !dlogits || (!dX && !dWg)) return MOE_ERR_INVALID_ARG;
+    if (!aligned(X, 16) || !aligned(Wg, 2) || !aligned(dlogits, 4) || (dX && !aligned(dX, 16)) ||
+        (dWg && !aligned(dWg, 4)))
+        return MOE_ERR_INVALID_ARG;
+    if (dWg) {
+        const size_t need = moe::gate_backward_workspace_bytes(p->T, p->d, p->E);
+        if (!workspace || workspace_bytes_given < need || !aligned(workspace, 256)) return MOE_ERR_WORKSPACE;
+    }
+    moe::GateBackArgs g{X, Wg, dlogits, dX, dWg, static_cast<float*>(workspace), p->T, p->d, p->E};
+    if (moe::launch_gate_backward(g, static_cast<hipStream_t>(stream)) != hipSuccess) return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
 const char* moe_route_strerror(int code) {
     switch (code) {
         case MOE_OK: return "success";

@@ -256,6 +256,16 @@ struct BiasArgs {
     float gamma;
 };
 
+struct GateBackArgs {
+    const uint16_t* X;       // [T,d] bf16 bits
+    const uint16_t* Wg;      // [d,E] bf16 bits
+    const float* dlogits;    // [T,E]
+    uint16_t* dX;            // [T,d] bf16 bits, or nullptr
+    float* dWg;              // [d,E], or nullptr
+    float* dWg_part;         // [slices,d,E] workspace
+    int T, d, E;
+};
+
 struct GateArgs {
     const uint16_t* X;
     const uint16_t* Wg;
@@ -281,6 +291,9 @@ int scatter_rows_per_wave(int E, int k);
 size_t scatter_lds_bytes(int E, int k);
 hipError_t launch_route_backward(const RowCfg& c, const BackArgs& a, hipStream_t st);
 hipError_t launch_bias_update(const BiasArgs& a, hipStream_t st);
+hipError_t launch_gate_backward(const GateBackArgs& a, hipStream_t st);
+int gate_backward_slices(int T, int d);
+size_t gate_backward_workspace_bytes(int T, int d, int E);
 hipError_t launch_gate_gemm(const GateArgs& a, uint16_t* wt, hipStream_t st);
 bool gate_supported(int T, int d, int E);
 size_t gate_workspace_bytes(int d, int E);

@@ -25,14 +25,15 @@ def lbs():
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_route\w*)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_(?:route|gate)\w*)\s*\(", src)))
 
 
 def test_every_declared_symbol_is_exported(lbs):
     lib = lbs.load()
     names = declared_functions()
     assert set(names) == {"moe_route", "moe_route_backward", "moe_route_bias_update",
-                          "moe_route_capacity", "moe_route_strerror", "moe_route_workspace_size"}
+                          "moe_route_capacity", "moe_route_strerror", "moe_route_workspace_size",
+                          "moe_gate_backward", "moe_gate_backward_workspace_size"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", lbs._binding.LIB_PATH],
@@ -150,3 +151,25 @@ def test_moe_route_validates_before_launching(lbs):
     assert bwd(ctypes.byref(pm), fake, None, fake, None, None, None, fake, None) == B.MOE_ERR_INVALID_ARG
     assert bwd(ctypes.byref(p), fake, None, fake, None, None, fake, fake, None) == B.MOE_ERR_INVALID_ARG
     assert bwd(ctypes.byref(p), fake, None, fake, None, fake + 2, fake, fake, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_gate_backward_validation(lbs):
+    """Shapes, pointers, alignment and workspace of the gate backward are
+    checked before any launch."""
+    lib = lbs.load()
+    B = lbs._binding
+    fake = 0x10000
+    p = lbs.make_params(64, 8, 2, d=64)
+    n = lbs.moe_gate_backward_workspace_size(p)
+    assert 0 < n < 64 * 1024 * 1024
+    gb = lib.moe_gate_backward
+    ok = (fake, fake, fake, fake, fake, fake, 1 << 20, None)
+    assert gb(ctypes.byref(lbs.make_params(64, 8, 2, d=0)), *ok) == B.MOE_ERR_INVALID_ARG
+    assert gb(ctypes.byref(lbs.make_params(64, 100, 2, d=64)), *ok) == B.MOE_ERR_UNSUPPORTED
+    assert gb(ctypes.byref(lbs.make_params(64, 8, 2, d=12)), *ok) == B.MOE_ERR_UNSUPPORTED
+    assert gb(ctypes.byref(p), None, fake, fake, fake, fake, fake, 1 << 20, None) == B.MOE_ERR_INVALID_ARG
+    assert gb(ctypes.byref(p), fake, fake, fake, None, None, fake, 1 << 20, None) == B.MOE_ERR_INVALID_ARG
+    assert gb(ctypes.byref(p), fake + 8, fake, fake, fake, fake, fake, 1 << 20, None) == B.MOE_ERR_INVALID_ARG
+    assert gb(ctypes.byref(p), fake, fake, fake, fake + 8, None, None, 0, None) == B.MOE_ERR_INVALID_ARG
+    assert gb(ctypes.byref(p), fake, fake, fake, None, fake, None, 0, None) == B.MOE_ERR_WORKSPACE
+    assert gb(ctypes.byref(p), fake, fake, fake, None, fake, fake, 16, None) == B.MOE_ERR_WORKSPACE
