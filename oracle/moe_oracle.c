@@ -19,6 +19,11 @@
  *        zero-count experts), 4.2 (distribution ratio, entropy).
  *   [p3] cnvsn.com/news/335486, survey of load balancing for large models:
  *        sections 3.1 and 5.1 (coefficient of variation, balance degree).
+ *   [p3] section 4.1.2 (EPLB): replicate_experts copies the expert with the
+ *        highest load per replica until the physical-expert count is reached;
+ *        balanced_packing sorts items by weight (descending) and puts each
+ *        into the lightest bin that is not full; worked example [9,7,5,3]
+ *        into 2 bins of 2 -> loads 12 and 12.
  *   [p1] section 4.3 also gives the loss-free variant: a per-expert scalar
  *        bias on the router logits, moved down for overloaded experts and up
  *        for idle ones (selection bias and its update, below).
@@ -402,4 +407,86 @@ void oracle_backward(const double *logits, long long T, long long E, long long k
     }
     free(p);
     free(G);
+}
+
+/*
+ * EPLB placement ([p3] 4.1.2), global strategy: replicate, then pack.
+ *
+ * replicate_experts: every logical expert starts with one replica; while
+ * the physical count is below num_phys, the expert with the largest load
+ * per replica weight[e] / logcnt[e] gets one more.  Physical expert i < E
+ * is logical i; replica E + r is the r-th copy made.  phy_rank[i] = the
+ * replica's number within its expert (0 for the original).
+ * balanced_packing: the physical replicas, weighted weight / logcnt of
+ * their expert (final counts), are sorted by weight descending and placed
+ * one by one into the lightest pack that holds fewer than
+ * num_phys / num_packs items; slot = its position in the pack.
+ * Readings: per-replica loads are compared exactly (cross-multiplied
+ * integers); ties in the replication and in the sort go to the lower index,
+ * ties between packs to the lower pack; pack loads are double sums
+ * accumulated in placement order.  Returns 0, or -1 on bad arguments.
+ */
+struct eplb_item { long long num, den; long long idx; };
+
+static int eplb_cmp_desc(const void *pa, const void *pb)
+{
+    const struct eplb_item *a = (const struct eplb_item *)pa;
+    const struct eplb_item *b = (const struct eplb_item *)pb;
+    long long l = a->num * b->den, r = b->num * a->den; /* a/b vs b's value */
+    if (l != r) return l > r ? -1 : 1;
+    return a->idx < b->idx ? -1 : (a->idx > b->idx ? 1 : 0);
+}
+
+int oracle_eplb(const int32_t *weight, long long E, long long num_phys, long long num_packs,
+                int32_t *phy2log, int32_t *phy_rank, int32_t *logcnt, int32_t *pack,
+                int32_t *slot, double *pack_load)
+{
+    if (E < 1 || num_phys < E || num_packs < 1 || num_phys % num_packs != 0)
+        return -1;
+    for (long long e = 0; e < E; ++e) {
+        if (weight[e] < 0) return -1;
+        phy2log[e] = (int32_t)e;
+        phy_rank[e] = 0;
+        logcnt[e] = 1;
+    }
+    for (long long i = E; i < num_phys; ++i) {
+        long long best = 0;
+        for (long long e = 1; e < E; ++e)
+            if ((long long)weight[e] * logcnt[best] > (long long)weight[best] * logcnt[e])
+                best = e;
+        phy2log[i] = (int32_t)best;
+        phy_rank[i] = logcnt[best];
+        logcnt[best] += 1;
+    }
+    struct eplb_item *it = (struct eplb_item *)malloc(sizeof(struct eplb_item) * (size_t)num_phys);
+    long long *cnt = (long long *)malloc(sizeof(long long) * (size_t)num_packs);
+    if (!it || !cnt) {
+        free(it); free(cnt);
+        return -1;
+    }
+    for (long long i = 0; i < num_phys; ++i) {
+        it[i].num = weight[phy2log[i]];
+        it[i].den = logcnt[phy2log[i]];
+        it[i].idx = i;
+    }
+    qsort(it, (size_t)num_phys, sizeof(struct eplb_item), eplb_cmp_desc);
+    const long long cap = num_phys / num_packs;
+    for (long long b = 0; b < num_packs; ++b) {
+        cnt[b] = 0;
+        pack_load[b] = 0.0;
+    }
+    for (long long n = 0; n < num_phys; ++n) {
+        long long best = -1;
+        for (long long b = 0; b < num_packs; ++b)
+            if (cnt[b] < cap && (best < 0 || pack_load[b] < pack_load[best]))
+                best = b;
+        const long long i = it[n].idx;
+        pack[i] = (int32_t)best;
+        slot[i] = (int32_t)cnt[best];
+        cnt[best] += 1;
+        pack_load[best] += (double)it[n].num / (double)it[n].den;
+    }
+    free(it);
+    free(cnt);
+    return 0;
 }

@@ -33,6 +33,8 @@ def load_library(path=None):
     lib.oracle_backward.restype = None
     lib.oracle_gate_backward.argtypes = [vp, vp, vp, ll, ll, ll, vp, vp]
     lib.oracle_gate_backward.restype = None
+    lib.oracle_eplb.argtypes = [vp, ll, ll, ll, vp, vp, vp, vp, vp, vp]
+    lib.oracle_eplb.restype = i
     lib.oracle_bias_update.argtypes = [vp, ll, ll, ll, ll, ctypes.c_float, vp]
     lib.oracle_bias_update.restype = None
     if path is None:
@@ -151,3 +153,19 @@ def bias_update(counts, T, k, gamma, bias, lib=None):
         raise ValueError("bias must have shape [E]")
     lib.oracle_bias_update(_p(cnt), m, E, int(T), int(k), float(gamma), _p(b))
     return b
+
+
+def eplb(weight, num_phys, num_packs, lib=None):
+    """EPLB placement of E logical experts with loads ``weight`` (ints) onto
+    ``num_phys`` physical replicas packed into ``num_packs`` equal packs."""
+    lib = lib or load_library()
+    w = np.ascontiguousarray(weight, dtype=np.int32).ravel()
+    E = w.shape[0]
+    o = dict(phy2log=np.empty(num_phys, np.int32), phy_rank=np.empty(num_phys, np.int32),
+             logcnt=np.empty(E, np.int32), pack=np.empty(num_phys, np.int32),
+             slot=np.empty(num_phys, np.int32), pack_load=np.empty(num_packs, np.float64))
+    rc = lib.oracle_eplb(_p(w), E, int(num_phys), int(num_packs),
+                         *[_p(o[n]) for n in ("phy2log", "phy_rank", "logcnt", "pack", "slot", "pack_load")])
+    if rc != 0:
+        raise ValueError("oracle_eplb rejected its arguments")
+    return o

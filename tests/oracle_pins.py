@@ -16,6 +16,9 @@ Pages (address, subject, section):
        balance degree 1 - (max-mean)/mean).
   [p1] 4.3 -- loss-free balancing: a per-expert scalar bias on the router
        logits, pushed down for overloaded experts and up for idle ones.
+  [p3] 4.1.2 -- EPLB: replicate_experts (copy the expert with the highest
+       load per replica) and balanced_packing (heaviest first into the
+       lightest non-full bin); worked example [9,7,5,3] -> 12 and 12.
 """
 import itertools
 import math
@@ -554,6 +557,110 @@ def pin_gate_backward_autograd(lib):
     (torch.tensor(G) * (Xt @ Wt)).sum().backward()
     assert np.allclose(dX, Xt.grad.numpy(), rtol=1e-13, atol=1e-16)
     assert np.allclose(dW, Wt.grad.numpy(), rtol=1e-12, atol=1e-13)  # sums of 29 terms
+
+
+# ------------------------------------------------------------ EPLB ([p3] 4.1.2)
+def _golden_lists(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                for tok in line.split():
+                    key, val = tok.split("=")
+                    vals[key] = [float(v) for v in val.split(",")]
+    return vals
+
+
+def _eplb_invariants(o, w, num_phys, packs):
+    E = len(w)
+    cap = num_phys // packs
+    assert sorted(o["phy2log"][:E]) == list(range(E))           # originals first
+    assert np.array_equal(np.bincount(o["phy2log"], minlength=E), o["logcnt"])
+    for e in range(E):                                            # replica numbers 0..logcnt-1
+        assert sorted(o["phy_rank"][o["phy2log"] == e]) == list(range(o["logcnt"][e]))
+    assert np.array_equal(np.bincount(o["pack"], minlength=packs), np.full(packs, cap))
+    for b in range(packs):
+        assert sorted(o["slot"][o["pack"] == b]) == list(range(cap))
+        members = np.flatnonzero(o["pack"] == b)
+        load = sum(w[o["phy2log"][i]] / o["logcnt"][o["phy2log"][i]] for i in members)
+        assert abs(o["pack_load"][b] - load) <= 1e-9 * max(1.0, load)
+
+
+def pin_eplb_worked_example(lib):
+    """[p3] 4.1.2: [9,7,5,3] over 2 packs of 2 -> 9,3 on pack 0 and 7,5 on
+    pack 1, both loaded 12 (tests/golden/eplb_worked_example.txt)."""
+    g = _golden_lists("eplb_worked_example.txt")
+    w = [int(v) for v in g["weights"]]
+    o = oracle.eplb(w, len(w), int(g["packs"][0]), lib=lib)
+    assert list(o["pack"]) == [int(v) for v in g["pack"]]
+    assert list(o["pack_load"]) == g["load"]
+    assert list(o["slot"]) == [0, 0, 1, 1]
+    _eplb_invariants(o, w, len(w), 2)
+
+
+def pin_eplb_hand_examples(lib):
+    """Traced by hand from the page's rules.  Replication of [10,6,3] to 5:
+    10/1 is largest -> copy 0 (10/2 = 5); then 6/1 -> copy 1.  Packing of
+    [4,4,2,2] into 2 packs: 4 -> pack 0, 4 -> pack 1 (lighter), 2 -> pack 0
+    (tie 4 = 4: lower pack), 2 -> pack 1 (pack 0 is full).  Ties in the sort
+    keep the lower index: [5,5] into 2 packs -> expert 0 on pack 0."""
+    o = oracle.eplb([10, 6, 3], 5, 1, lib=lib)
+    assert list(o["phy2log"]) == [0, 1, 2, 0, 1] and list(o["phy_rank"]) == [0, 0, 0, 1, 1]
+    assert list(o["logcnt"]) == [2, 2, 1]
+    assert list(o["pack_load"]) == [5.0 + 5.0 + 3.0 + 3.0 + 3.0]
+    o = oracle.eplb([4, 4, 2, 2], 4, 2, lib=lib)
+    assert list(o["pack"]) == [0, 1, 0, 1] and list(o["pack_load"]) == [6.0, 6.0]
+    o = oracle.eplb([5, 5], 2, 2, lib=lib)
+    assert list(o["pack"]) == [0, 1]
+    # replicas of one expert: 12 copied twice -> three replicas of 4 each
+    o = oracle.eplb([12, 1], 4, 2, lib=lib)
+    assert list(o["phy2log"]) == [0, 1, 0, 0] and list(o["logcnt"]) == [3, 1]
+    # items 4 (x3, phys 0,2,3) and 1: 4 -> p0, 4 -> p1, 4 -> p0, 1 -> p1
+    assert list(o["pack"]) == [0, 1, 1, 0] and list(o["pack_load"]) == [8.0, 5.0]
+
+
+def pin_eplb_replication_optimal(lib):
+    """The replication greedy minimises the largest load per replica
+    max_e w_e / c_e over all ways of giving R extra replicas to E experts
+    (brute force over every distribution, tiny sizes)."""
+    rng = np.random.default_rng(27)
+    for _ in range(40):
+        E = int(rng.integers(1, 5))
+        R = int(rng.integers(0, 5))
+        w = rng.integers(0, 20, size=E)
+        o = oracle.eplb(w, E + R, 1, lib=lib)
+        got = max(w[e] / o["logcnt"][e] for e in range(E))
+        best = min(max(w[e] / (1 + extra[e]) for e in range(E))
+                   for extra in itertools.product(range(R + 1), repeat=E) if sum(extra) == R)
+        assert abs(got - best) < 1e-12, (w, R, got, best)
+        _eplb_invariants(o, w, E + R, 1)
+
+
+def pin_eplb_packing_properties(lib):
+    """Packing: equal counts per pack, loads equal their members' weights,
+    the heaviest item sits alone at the head of pack 0, equal weights spread
+    evenly, and the greedy's largest pack load is within the longest-
+    processing-time bound 4/3 of the brute-force optimum (tiny sizes)."""
+    rng = np.random.default_rng(28)
+    for _ in range(30):
+        packs = int(rng.integers(1, 4))
+        cap = int(rng.integers(1, 4))
+        n = packs * cap
+        w = rng.integers(1, 30, size=n)
+        o = oracle.eplb(w, n, packs, lib=lib)
+        _eplb_invariants(o, w, n, packs)
+        top = int(np.lexsort((np.arange(n), -w))[0])
+        assert o["pack"][top] == 0 and o["slot"][top] == 0
+        best = None
+        for assign in itertools.product(range(packs), repeat=n):
+            if np.all(np.bincount(assign, minlength=packs) == cap):
+                m = max(sum(w[i] for i in range(n) if assign[i] == b) for b in range(packs))
+                best = m if best is None else min(best, m)
+        assert max(o["pack_load"]) >= best - 1e-9
+        assert max(o["pack_load"]) <= 4.0 / 3.0 * best + 1e-9, (w, packs, o["pack_load"], best)
+    o = oracle.eplb(np.full(12, 7), 12, 4, lib=lib)
+    assert np.all(o["pack_load"] == 21.0)
 
 
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

@@ -68,6 +68,16 @@ MUTANTS = {
                               "acc += dlogits[t * E + e] * bf16_to_double(Wg[(e * d + i) % (d * E)]);"),
     "gate_dWg_wrong_row": ("acc += bf16_to_double(X[t * d + i]) * dlogits[t * E + e];",
                            "acc += bf16_to_double(X[t * d + (i + 1) % d]) * dlogits[t * E + e];"),
+    "eplb_replicate_by_weight": ("if ((long long)weight[e] * logcnt[best] > (long long)weight[best] * logcnt[e])",
+                                 "if ((long long)weight[e] > (long long)weight[best])"),
+    "eplb_sort_ascending": ("if (l != r) return l > r ? -1 : 1;", "if (l != r) return l > r ? 1 : -1;"),
+    "eplb_heaviest_pack": ("if (cnt[b] < cap && (best < 0 || pack_load[b] < pack_load[best]))",
+                           "if (cnt[b] < cap && (best < 0 || pack_load[b] > pack_load[best]))"),
+    "eplb_ignores_full": ("if (cnt[b] < cap && (best < 0 || pack_load[b] < pack_load[best]))",
+                          "if ((best < 0 || pack_load[b] < pack_load[best]))"),
+    "eplb_pack_tie_higher": ("if (cnt[b] < cap && (best < 0 || pack_load[b] < pack_load[best]))",
+                             "if (cnt[b] < cap && (best < 0 || pack_load[b] <= pack_load[best]))"),
+    "eplb_item_weight_not_per_replica": ("it[i].den = logcnt[phy2log[i]];", "it[i].den = 1;"),
     "bias_ignored": ("topk_row(selrow, E, k, idx, taken);",
                      "topk_row(row, E, k, idx, taken);"),
     "bias_added_in_double": ("selrow[e] = (double)biased;",
