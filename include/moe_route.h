@@ -15,6 +15,8 @@
  *        (coefficient of variation, load-balance degree).
  *   [p1] 4.3 -- loss-free balancing: a per-expert scalar bias on the router
  *        logits, moved down for overloaded experts and up for idle ones.
+ *   [p3] 4.1.2 -- EPLB: replicate heavily loaded experts, pack the replicas
+ *        onto GPUs (balanced_packing).
  *
  * Conventions shared by every entry point:
  *   - Every array pointer is a DEVICE pointer to memory that the caller
@@ -220,6 +222,32 @@ int moe_gate_backward_workspace_size(const moe_route_params *p, size_t *bytes);
 int moe_gate_backward(const moe_route_params *p, const uint16_t *X, const uint16_t *Wg,
                       const float *dlogits, uint16_t *dX, float *dWg, void *workspace,
                       size_t workspace_bytes, void *stream);
+
+/*
+ * EPLB placement over expert loads ([p3] 4.1.2, global strategy), one
+ * workgroup:
+ *   replicate_experts: every expert starts with one replica; while fewer
+ *   than num_phys replicas exist, the expert with the largest load per
+ *   replica weight[e] / logcnt[e] gets another.  Physical replica i < E is
+ *   expert i; replica E + r is the r-th copy made.
+ *   balanced_packing: the replicas, each weighted weight / logcnt of its
+ *   expert, are placed heaviest first into the lightest pack (GPU) that
+ *   holds fewer than num_phys / num_packs replicas.
+ * Per-replica loads compare exactly; ties go to the lower expert, replica
+ * and pack index.  weight [E] int32 >= 0 (e.g. a row of moe_route's
+ * counts; negative values count as 0).  Outputs: phy2log [num_phys]
+ * (expert of each replica), phy_rank [num_phys] (replica number within its
+ * expert), logcnt [E] (replicas per expert), pack [num_phys] and slot
+ * [num_phys] (the replica's pack and position in it), pack_load
+ * [num_packs] fp64 (8-byte aligned).
+ * Limits: 1 <= E <= MOE_ROUTE_MAX_E, E <= num_phys <= MOE_EPLB_MAX_PHYS,
+ * 1 <= num_packs <= MOE_EPLB_MAX_PACKS, num_phys % num_packs == 0.
+ */
+#define MOE_EPLB_MAX_PHYS  4096
+#define MOE_EPLB_MAX_PACKS 1024
+int moe_eplb_plan(int32_t E, int32_t num_phys, int32_t num_packs, const int32_t *weight,
+                  int32_t *phy2log, int32_t *phy_rank, int32_t *logcnt, int32_t *pack,
+                  int32_t *slot, double *pack_load, void *stream);
 
 /* Static message for a return code. */
 const char *moe_route_strerror(int code);

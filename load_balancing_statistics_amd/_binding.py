@@ -88,6 +88,9 @@ def load(path=None):
     lib.moe_gate_backward_workspace_size.restype = ctypes.c_int
     lib.moe_gate_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.moe_gate_backward.restype = ctypes.c_int
+    i32 = ctypes.c_int32
+    lib.moe_eplb_plan.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.moe_eplb_plan.restype = ctypes.c_int
     lib.moe_route_strerror.argtypes = [ctypes.c_int]
     lib.moe_route_strerror.restype = ctypes.c_char_p
     if path is None:
@@ -191,6 +194,27 @@ def moe_gate_backward(params, X, Wg, dlogits, dX=None, dWg=None, workspace=None,
                                   _ptr(dWg), _ptr(workspace), nbytes, _stream(stream))
     if rc != MOE_OK:
         raise MoeRouteError(rc, "moe_gate_backward")
+
+
+def moe_eplb_plan(weight, num_phys, num_packs, stream=None):
+    """EPLB placement of the experts with loads ``weight`` (int32 device tensor
+    [E]); returns a dict of device tensors named like the C outputs."""
+    import torch
+    E = weight.numel()
+    dev = weight.device
+    i32 = torch.int32
+    o = dict(phy2log=torch.empty(num_phys, dtype=i32, device=dev),
+             phy_rank=torch.empty(num_phys, dtype=i32, device=dev),
+             logcnt=torch.empty(E, dtype=i32, device=dev),
+             pack=torch.empty(num_phys, dtype=i32, device=dev),
+             slot=torch.empty(num_phys, dtype=i32, device=dev),
+             pack_load=torch.empty(num_packs, dtype=torch.float64, device=dev))
+    rc = load().moe_eplb_plan(E, int(num_phys), int(num_packs), _ptr(weight),
+                              *[_ptr(o[n]) for n in ("phy2log", "phy_rank", "logcnt", "pack", "slot",
+                                                     "pack_load")], _stream(stream))
+    if rc != MOE_OK:
+        raise MoeRouteError(rc, "moe_eplb_plan")
+    return o
 
 
 def alloc_outputs(params, device="cuda"):

@@ -262,6 +262,21 @@ int moe_gate_backward(const moe_route_params* p, const uint16_t* X, const uint16
     return MOE_OK;
 }
 
+int moe_eplb_plan(int32_t E, int32_t num_phys, int32_t num_packs, const int32_t* weight,
+                  int32_t* phy2log, int32_t* phy_rank, int32_t* logcnt, int32_t* pack, int32_t* slot,
+                  double* pack_load, void* stream) {
+    if (E < 1 || num_phys < E || num_packs < 1 || num_phys % num_packs != 0) return MOE_ERR_INVALID_ARG;
+    if (E > MOE_ROUTE_MAX_E || num_phys > MOE_EPLB_MAX_PHYS || num_packs > MOE_EPLB_MAX_PACKS)
+        return MOE_ERR_UNSUPPORTED;
+    const void* ptrs[] = {weight, phy2log, phy_rank, logcnt, pack, slot};
+    for (const void* q : ptrs)
+        if (!q || !aligned(q, 4)) return MOE_ERR_INVALID_ARG;
+    if (!pack_load || !aligned(pack_load, 8)) return MOE_ERR_INVALID_ARG;
+    moe::EplbArgs e{weight, phy2log, phy_rank, logcnt, pack, slot, pack_load, E, num_phys, num_packs};
+    if (moe::launch_eplb(e, static_cast<hipStream_t>(stream)) != hipSuccess) return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
 const char* moe_route_strerror(int code) {
     switch (code) {
         case MOE_OK: return "success";

@@ -266,6 +266,17 @@ struct GateBackArgs {
     int T, d, E;
 };
 
+struct EplbArgs {
+    const int32_t* weight;  // [E] loads (e.g. one row of moe_route's counts)
+    int32_t* phy2log;       // [P]
+    int32_t* phy_rank;      // [P]
+    int32_t* logcnt;        // [E]
+    int32_t* pack;          // [P]
+    int32_t* slot;          // [P]
+    double* pack_load;      // [num_packs]
+    int E, num_phys, num_packs;
+};
+
 struct GateArgs {
     const uint16_t* X;
     const uint16_t* Wg;
@@ -292,6 +303,8 @@ size_t scatter_lds_bytes(int E, int k);
 hipError_t launch_route_backward(const RowCfg& c, const BackArgs& a, hipStream_t st);
 hipError_t launch_bias_update(const BiasArgs& a, hipStream_t st);
 hipError_t launch_gate_backward(const GateBackArgs& a, hipStream_t st);
+hipError_t launch_eplb(const EplbArgs& a, hipStream_t st);
+size_t eplb_lds_bytes(int E, int num_phys);
 int gate_backward_slices(int T, int d);
 size_t gate_backward_workspace_bytes(int T, int d, int E);
 hipError_t launch_gate_gemm(const GateArgs& a, uint16_t* wt, hipStream_t st);

@@ -25,7 +25,7 @@ def lbs():
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_(?:route|gate)\w*)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_(?:route|gate|eplb)\w*)\s*\(", src)))
 
 
 def test_every_declared_symbol_is_exported(lbs):
@@ -33,7 +33,7 @@ def test_every_declared_symbol_is_exported(lbs):
     names = declared_functions()
     assert set(names) == {"moe_route", "moe_route_backward", "moe_route_bias_update",
                           "moe_route_capacity", "moe_route_strerror", "moe_route_workspace_size",
-                          "moe_gate_backward", "moe_gate_backward_workspace_size"}
+                          "moe_gate_backward", "moe_gate_backward_workspace_size", "moe_eplb_plan"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", lbs._binding.LIB_PATH],
@@ -173,3 +173,17 @@ def test_gate_backward_validation(lbs):
     assert gb(ctypes.byref(p), fake, fake, fake, fake + 8, None, None, 0, None) == B.MOE_ERR_INVALID_ARG
     assert gb(ctypes.byref(p), fake, fake, fake, None, fake, None, 0, None) == B.MOE_ERR_WORKSPACE
     assert gb(ctypes.byref(p), fake, fake, fake, None, fake, fake, 16, None) == B.MOE_ERR_WORKSPACE
+
+
+def test_eplb_validation(lbs):
+    lib = lbs.load()
+    B = lbs._binding
+    f = 0x10000
+    ok = (f, f, f, f, f, f, f)
+    assert lib.moe_eplb_plan(0, 4, 2, *ok, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_eplb_plan(8, 4, 2, *ok, None) == B.MOE_ERR_INVALID_ARG      # num_phys < E
+    assert lib.moe_eplb_plan(4, 6, 4, *ok, None) == B.MOE_ERR_INVALID_ARG      # not divisible
+    assert lib.moe_eplb_plan(2048, 4096, 2, *ok, None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_eplb_plan(4, 8192, 2, *ok, None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_eplb_plan(4, 8, 2, None, f, f, f, f, f, f, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_eplb_plan(4, 8, 2, f, f, f, f, f, f, f + 4, None) == B.MOE_ERR_INVALID_ARG  # fp64 alignment
