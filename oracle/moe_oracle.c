@@ -24,6 +24,11 @@
  *        balanced_packing sorts items by weight (descending) and puts each
  *        into the lightest bin that is not full; worked example [9,7,5,3]
  *        into 2 bins of 2 -> loads 12 and 12.
+ *   [p4] baidu-baige.github.io LoongForge blog on TAOT (topology-aware optimal
+ *        transport for expert replicas), section 2 Phase 1: overload of each
+ *        rank as supply, idle capacity as demand, a topology cost matrix, and
+ *        the entropy-regularised plan T = diag(u) K diag(v) computed by
+ *        alternating Sinkhorn-Knopp matrix-vector steps (about 50 rounds).
  *   [p1] section 4.3 also gives the loss-free variant: a per-expert scalar
  *        bias on the router logits, moved down for overloaded experts and up
  *        for idle ones (selection bias and its update, below).
@@ -488,5 +493,52 @@ int oracle_eplb(const int32_t *weight, long long E, long long num_phys, long lon
     }
     free(it);
     free(cnt);
+    return 0;
+}
+
+/*
+ * Sinkhorn-Knopp flow plan ([p4] section 2, Phase 1).  supply a [R],
+ * demand b [R] (a and b should carry the same total), cost C [R*R]
+ * row-major, regularisation eps > 0.  Gibbs kernel K = exp(-C / eps);
+ * starting from u = v = 1, each of the iters rounds sets
+ *   u_i = a_i / max(sum_j K_ij v_j, tiny),  then
+ *   v_j = b_j / max(sum_i K_ij u_i, tiny),
+ * sums taken in index order, tiny = 1e-300 (the page's clamp; reading).
+ * Outputs u [R], v [R] and the plan T [R*R], T_ij = u_i K_ij v_j.
+ * Returns 0, or -1 on bad arguments.
+ */
+int oracle_sinkhorn(const double *a, const double *b, const double *C, long long R, double eps,
+                    long long iters, double *u, double *v, double *T)
+{
+    if (R < 1 || !(eps > 0.0) || iters < 0)
+        return -1;
+    double *K = (double *)malloc(sizeof(double) * (size_t)(R * R));
+    if (!K)
+        return -1;
+    for (long long i = 0; i < R * R; ++i)
+        K[i] = exp(-C[i] / eps);
+    for (long long i = 0; i < R; ++i) {
+        u[i] = 1.0;
+        v[i] = 1.0;
+    }
+    const double tiny = 1e-300;
+    for (long long it = 0; it < iters; ++it) {
+        for (long long i = 0; i < R; ++i) {
+            double s = 0.0;
+            for (long long j = 0; j < R; ++j)
+                s += K[i * R + j] * v[j];
+            u[i] = a[i] / (s > tiny ? s : tiny);
+        }
+        for (long long j = 0; j < R; ++j) {
+            double s = 0.0;
+            for (long long i = 0; i < R; ++i)
+                s += K[i * R + j] * u[i];
+            v[j] = b[j] / (s > tiny ? s : tiny);
+        }
+    }
+    for (long long i = 0; i < R; ++i)
+        for (long long j = 0; j < R; ++j)
+            T[i * R + j] = u[i] * K[i * R + j] * v[j];
+    free(K);
     return 0;
 }

@@ -35,6 +35,8 @@ def load_library(path=None):
     lib.oracle_gate_backward.restype = None
     lib.oracle_eplb.argtypes = [vp, ll, ll, ll, vp, vp, vp, vp, vp, vp]
     lib.oracle_eplb.restype = i
+    lib.oracle_sinkhorn.argtypes = [vp, vp, vp, ll, d, ll, vp, vp, vp]
+    lib.oracle_sinkhorn.restype = i
     lib.oracle_bias_update.argtypes = [vp, ll, ll, ll, ll, ctypes.c_float, vp]
     lib.oracle_bias_update.restype = None
     if path is None:
@@ -169,3 +171,17 @@ def eplb(weight, num_phys, num_packs, lib=None):
     if rc != 0:
         raise ValueError("oracle_eplb rejected its arguments")
     return o
+
+
+def sinkhorn(a, b, C, eps, iters=50, lib=None):
+    """Sinkhorn-Knopp plan for supply ``a`` [R], demand ``b`` [R], cost ``C`` [R,R]:
+    returns (T [R,R], u [R], v [R]) in float64."""
+    lib = lib or load_library()
+    a = np.ascontiguousarray(a, dtype=np.float64).ravel()
+    b = np.ascontiguousarray(b, dtype=np.float64).ravel()
+    R = a.shape[0]
+    Cm = np.ascontiguousarray(C, dtype=np.float64).reshape(R, R)
+    u, v, T = np.empty(R), np.empty(R), np.empty((R, R))
+    if lib.oracle_sinkhorn(_p(a), _p(b), _p(Cm), R, float(eps), int(iters), _p(u), _p(v), _p(T)) != 0:
+        raise ValueError("oracle_sinkhorn rejected its arguments")
+    return T, u, v

@@ -16,6 +16,8 @@ Pages (address, subject, section):
        balance degree 1 - (max-mean)/mean).
   [p1] 4.3 -- loss-free balancing: a per-expert scalar bias on the router
        logits, pushed down for overloaded experts and up for idle ones.
+  [p4] LoongForge TAOT blog, section 2 Phase 1 -- Sinkhorn-Knopp plan
+       T = diag(u) K diag(v) between supply and demand under a cost matrix.
   [p3] 4.1.2 -- EPLB: replicate_experts (copy the expert with the highest
        load per replica) and balanced_packing (heaviest first into the
        lightest non-full bin); worked example [9,7,5,3] -> 12 and 12.
@@ -661,6 +663,49 @@ def pin_eplb_packing_properties(lib):
         assert max(o["pack_load"]) <= 4.0 / 3.0 * best + 1e-9, (w, packs, o["pack_load"], best)
     o = oracle.eplb(np.full(12, 7), 12, 4, lib=lib)
     assert np.all(o["pack_load"] == 21.0)
+
+
+# ------------------------------------------------------- Sinkhorn ([p4] 2)
+def pin_sinkhorn_2x2_closed_form(lib):
+    """For R = 2 with equal totals the plan has one free entry t = T_11; the
+    Gibbs structure fixes the cross ratio T11 T22 / (T12 T21) = K11 K22 /
+    (K12 K21) = rho, so t solves (1-rho) t^2 + (a2 - b1 + rho (a1 + b1)) t
+    - rho a1 b1 = 0.  Converged Sinkhorn equals that root."""
+    for a, b, C, eps in [([3.0, 1.0], [2.0, 2.0], [[0.0, 1.0], [1.0, 0.0]], 0.7),
+                         ([0.5, 2.5], [1.0, 2.0], [[0.2, 1.5], [0.9, 0.1]], 1.3),
+                         ([4.0, 4.0], [1.0, 7.0], [[1.0, 0.0], [0.0, 2.0]], 0.5)]:
+        T, u, v = oracle.sinkhorn(a, b, C, eps, iters=400, lib=lib)
+        K = np.exp(-np.asarray(C) / eps)
+        rho = K[0, 0] * K[1, 1] / (K[0, 1] * K[1, 0])
+        qa, qb, qc = 1 - rho, a[1] - b[0] + rho * (a[0] + b[0]), -rho * a[0] * b[0]
+        roots = np.roots([qa, qb, qc]) if abs(qa) > 1e-15 else np.array([-qc / qb])
+        lo, hi = max(0.0, b[0] - a[1]), min(a[0], b[0])
+        t = [r.real for r in roots if abs(r.imag) < 1e-12 and lo - 1e-12 <= r.real <= hi + 1e-12]
+        assert len(t) == 1
+        want = np.array([[t[0], a[0] - t[0]], [b[0] - t[0], a[1] - b[0] + t[0]]])
+        assert np.allclose(T, want, rtol=1e-10, atol=1e-12), (T, want)
+
+
+def pin_sinkhorn_marginals_and_structure(lib):
+    """After the rounds the column sums equal the demand (the last step is
+    the v update), the row sums converge to the supply, and T_ij / (u_i v_j)
+    is the Gibbs kernel exp(-C_ij / eps).  A constant cost gives the
+    independent coupling a b^T / sum(a) after one round."""
+    rng = np.random.default_rng(29)
+    for R in [3, 8, 64]:
+        a = rng.random(R) + 0.1
+        b = rng.random(R) + 0.1
+        b *= a.sum() / b.sum()
+        C = rng.random((R, R)) * 2
+        T, u, v = oracle.sinkhorn(a, b, C, 0.5, iters=300, lib=lib)
+        assert np.allclose(T.sum(0), b, rtol=1e-12)
+        assert np.allclose(T.sum(1), a, rtol=1e-8)
+        assert np.allclose(T / np.outer(u, v), np.exp(-C / 0.5), rtol=1e-12)
+        T1, _, _ = oracle.sinkhorn(a, b, np.full((R, R), 0.8), 0.3, iters=1, lib=lib)
+        assert np.allclose(T1, np.outer(a, b) / a.sum(), rtol=1e-12)
+    # zero iterations: u = v = 1, T = K
+    T0, u0, v0 = oracle.sinkhorn([1.0, 2.0], [2.0, 1.0], [[0.0, 1.0], [2.0, 3.0]], 2.0, iters=0, lib=lib)
+    assert np.allclose(T0, np.exp(-np.array([[0.0, 1.0], [2.0, 3.0]]) / 2.0), rtol=1e-15)
 
 
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

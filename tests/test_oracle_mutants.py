@@ -78,6 +78,9 @@ MUTANTS = {
     "eplb_pack_tie_higher": ("if (cnt[b] < cap && (best < 0 || pack_load[b] < pack_load[best]))",
                              "if (cnt[b] < cap && (best < 0 || pack_load[b] <= pack_load[best]))"),
     "eplb_item_weight_not_per_replica": ("it[i].den = logcnt[phy2log[i]];", "it[i].den = 1;"),
+    "sinkhorn_kernel_sign": ("K[i] = exp(-C[i] / eps);", "K[i] = exp(C[i] / eps);"),
+    "sinkhorn_u_uses_column": ("s += K[i * R + j] * v[j];", "s += K[j * R + i] * v[j];"),
+    "sinkhorn_v_from_old_u": ("u[i] = a[i] / (s > tiny ? s : tiny);", "u[i] = (it == 0) ? a[i] / (s > tiny ? s : tiny) : u[i];"),
     "bias_ignored": ("topk_row(selrow, E, k, idx, taken);",
                      "topk_row(row, E, k, idx, taken);"),
     "bias_added_in_double": ("selrow[e] = (double)biased;",
