@@ -17,6 +17,8 @@
  *        logits, moved down for overloaded experts and up for idle ones.
  *   [p3] 4.1.2 -- EPLB: replicate heavily loaded experts, pack the replicas
  *        onto GPUs (balanced_packing).
+ *   [p4] baidu-baige.github.io LoongForge blog on TAOT, section 2 Phase 1 --
+ *        Sinkhorn-Knopp transport plan between overloaded and idle ranks.
  *
  * Conventions shared by every entry point:
  *   - Every array pointer is a DEVICE pointer to memory that the caller
@@ -248,6 +250,22 @@ int moe_gate_backward(const moe_route_params *p, const uint16_t *X, const uint16
 int moe_eplb_plan(int32_t E, int32_t num_phys, int32_t num_packs, const int32_t *weight,
                   int32_t *phy2log, int32_t *phy_rank, int32_t *logcnt, int32_t *pack,
                   int32_t *slot, double *pack_load, void *stream);
+
+/*
+ * Sinkhorn-Knopp flow plan ([p4] TAOT section 2, Phase 1), one wave:
+ * supply a [R] (each rank's overload), demand b [R] (idle capacity; the
+ * totals should be equal), cost [R,R] row-major (topology cost between
+ * ranks), eps > 0 the entropy regularisation.  Gibbs kernel
+ * K = exp(-cost / eps); from u = v = 1, each of the iters rounds sets
+ *   u_i = a_i / max(sum_j K_ij v_j, 1e-300), then v_j = b_j / max(sum_i K_ij u_i, 1e-300);
+ * outputs u [R], v [R] and the plan T [R,R] = diag(u) K diag(v).  All fp64,
+ * 8-byte aligned.  Limits: 1 <= R <= MOE_SINKHORN_MAX_R,
+ * 0 <= iters <= MOE_SINKHORN_MAX_ITERS.
+ */
+#define MOE_SINKHORN_MAX_R     64
+#define MOE_SINKHORN_MAX_ITERS 100000
+int moe_sinkhorn_plan(int32_t R, const double *supply, const double *demand, const double *cost,
+                      double eps, int32_t iters, double *u, double *v, double *T, void *stream);
 
 /* Static message for a return code. */
 const char *moe_route_strerror(int code);

@@ -91,6 +91,8 @@ def load(path=None):
     i32 = ctypes.c_int32
     lib.moe_eplb_plan.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_eplb_plan.restype = ctypes.c_int
+    lib.moe_sinkhorn_plan.argtypes = [i32, vp, vp, vp, ctypes.c_double, i32, vp, vp, vp, vp]
+    lib.moe_sinkhorn_plan.restype = ctypes.c_int
     lib.moe_route_strerror.argtypes = [ctypes.c_int]
     lib.moe_route_strerror.restype = ctypes.c_char_p
     if path is None:
@@ -215,6 +217,22 @@ def moe_eplb_plan(weight, num_phys, num_packs, stream=None):
     if rc != MOE_OK:
         raise MoeRouteError(rc, "moe_eplb_plan")
     return o
+
+
+def moe_sinkhorn_plan(supply, demand, cost, eps, iters=50, stream=None):
+    """Sinkhorn-Knopp plan from fp64 device tensors supply [R], demand [R], cost
+    [R,R]; returns (T [R,R], u [R], v [R]) as fp64 device tensors."""
+    import torch
+    R = supply.numel()
+    dev = supply.device
+    u = torch.empty(R, dtype=torch.float64, device=dev)
+    v = torch.empty(R, dtype=torch.float64, device=dev)
+    T = torch.empty((R, R), dtype=torch.float64, device=dev)
+    rc = load().moe_sinkhorn_plan(R, _ptr(supply), _ptr(demand), _ptr(cost), float(eps), int(iters),
+                                  _ptr(u), _ptr(v), _ptr(T), _stream(stream))
+    if rc != MOE_OK:
+        raise MoeRouteError(rc, "moe_sinkhorn_plan")
+    return T, u, v
 
 
 def alloc_outputs(params, device="cuda"):

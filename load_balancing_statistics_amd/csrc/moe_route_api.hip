@@ -277,6 +277,18 @@ int moe_eplb_plan(int32_t E, int32_t num_phys, int32_t num_packs, const int32_t*
     return MOE_OK;
 }
 
+int moe_sinkhorn_plan(int32_t R, const double* supply, const double* demand, const double* cost,
+                      double eps, int32_t iters, double* u, double* v, double* T, void* stream) {
+    if (R < 1 || iters < 0 || !(eps > 0.0) || !std::isfinite(eps)) return MOE_ERR_INVALID_ARG;
+    if (R > MOE_SINKHORN_MAX_R || iters > MOE_SINKHORN_MAX_ITERS) return MOE_ERR_UNSUPPORTED;
+    const void* ptrs[] = {supply, demand, cost, u, v, T};
+    for (const void* q : ptrs)
+        if (!q || !aligned(q, 8)) return MOE_ERR_INVALID_ARG;
+    moe::SinkhornArgs k{supply, demand, cost, u, v, T, eps, R, iters};
+    if (moe::launch_sinkhorn(k, static_cast<hipStream_t>(stream)) != hipSuccess) return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
 const char* moe_route_strerror(int code) {
     switch (code) {
         case MOE_OK: return "success";

@@ -277,6 +277,17 @@ struct EplbArgs {
     int E, num_phys, num_packs;
 };
 
+struct SinkhornArgs {
+    const double* supply;  // [R]
+    const double* demand;  // [R]
+    const double* C;       // [R,R]
+    double* u;             // [R]
+    double* v;             // [R]
+    double* T;             // [R,R]
+    double eps;
+    int R, iters;
+};
+
 struct GateArgs {
     const uint16_t* X;
     const uint16_t* Wg;
@@ -304,6 +315,7 @@ hipError_t launch_route_backward(const RowCfg& c, const BackArgs& a, hipStream_t
 hipError_t launch_bias_update(const BiasArgs& a, hipStream_t st);
 hipError_t launch_gate_backward(const GateBackArgs& a, hipStream_t st);
 hipError_t launch_eplb(const EplbArgs& a, hipStream_t st);
+hipError_t launch_sinkhorn(const SinkhornArgs& a, hipStream_t st);
 size_t eplb_lds_bytes(int E, int num_phys);
 int gate_backward_slices(int T, int d);
 size_t gate_backward_workspace_bytes(int T, int d, int E);

@@ -25,7 +25,7 @@ def lbs():
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_(?:route|gate|eplb)\w*)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(moe_(?:route|gate|eplb|sinkhorn)\w*)\s*\(", src)))
 
 
 def test_every_declared_symbol_is_exported(lbs):
@@ -33,7 +33,8 @@ def test_every_declared_symbol_is_exported(lbs):
     names = declared_functions()
     assert set(names) == {"moe_route", "moe_route_backward", "moe_route_bias_update",
                           "moe_route_capacity", "moe_route_strerror", "moe_route_workspace_size",
-                          "moe_gate_backward", "moe_gate_backward_workspace_size", "moe_eplb_plan"}
+                          "moe_gate_backward", "moe_gate_backward_workspace_size", "moe_eplb_plan",
+                          "moe_sinkhorn_plan"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", lbs._binding.LIB_PATH],
@@ -187,3 +188,18 @@ def test_eplb_validation(lbs):
     assert lib.moe_eplb_plan(4, 8192, 2, *ok, None) == B.MOE_ERR_UNSUPPORTED
     assert lib.moe_eplb_plan(4, 8, 2, None, f, f, f, f, f, f, None) == B.MOE_ERR_INVALID_ARG
     assert lib.moe_eplb_plan(4, 8, 2, f, f, f, f, f, f, f + 4, None) == B.MOE_ERR_INVALID_ARG  # fp64 alignment
+
+
+def test_sinkhorn_validation(lbs):
+    lib = lbs.load()
+    B = lbs._binding
+    f = 0x10000
+    ok = (f, f, f)
+    outs = (f, f, f)
+    assert lib.moe_sinkhorn_plan(0, *ok, 1.0, 50, *outs, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_sinkhorn_plan(65, *ok, 1.0, 50, *outs, None) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_sinkhorn_plan(8, *ok, 0.0, 50, *outs, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_sinkhorn_plan(8, *ok, float("inf"), 50, *outs, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_sinkhorn_plan(8, *ok, 1.0, -1, *outs, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_sinkhorn_plan(8, f, f, None, 1.0, 50, *outs, None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_sinkhorn_plan(8, f + 4, f, f, 1.0, 50, *outs, None) == B.MOE_ERR_INVALID_ARG
