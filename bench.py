@@ -10,6 +10,10 @@ rotated over several copies (> 512 MB in total) so that the 256 MB Infinity
 Cache cannot serve them.  Prints ONE JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload v3_shape]
+
+Workloads: switch_top1, zipf_top2, gate_top2, v3_shape (default), v4_shape,
+v3_select_bias; and the two planners, eplb_v4 and sinkhorn_r64, which print
+their per-call latency instead.
 """
 import argparse
 import ctypes
@@ -169,12 +173,85 @@ def cpu_baseline(w, inp, budget_s):
             "sample": sample, "seconds": round(elapsed, 2)}
 
 
+PLANNERS = ("eplb_v4", "sinkhorn_r64")
+
+
+def planner_bench(args):
+    """Latency of one planner call (EPLB placement over a v4_shape microbatch's
+    counts: 384 experts, 64 extra replicas, 64 GPUs; or the Sinkhorn plan for
+    64 ranks in nodes of 8, 50 rounds), GPU events around K back-to-back
+    calls, with the oracle timed on the same input."""
+    import numpy as np
+    import torch
+    import load_balancing_statistics_amd as lbs
+    from load_balancing_statistics_amd.workloads import WORKLOADS, make_inputs
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    K = args.steps
+    if args.workload == "eplb_v4":
+        w = WORKLOADS["v4_shape"]
+        inp = make_inputs(w, 0)
+        p = lbs.make_params(w.T, w.E, w.k, n_micro=w.n_micro, capacity_factor=w.capacity_factor,
+                            alpha=w.alpha, renorm=w.renorm)
+        out = lbs.alloc_outputs(p, device=dev)
+        ws = lbs.alloc_workspace(p, device=dev)
+        lbs.moe_route(p, out, ws, logits=torch.from_numpy(inp["logits"]).to(dev))
+        weight = out["counts"][0].contiguous()
+        cfg = {"workload": "eplb_v4", "E": w.E, "num_phys": w.E + 64, "num_packs": 64}
+        call = lambda: lbs.moe_eplb_plan(weight, w.E + 64, 64)
+        host_w = weight.cpu().numpy()
+        cpu_call = lambda: __import__("oracle").eplb(host_w, w.E + 64, 64)
+    else:
+        R, per_node, lam = 64, 8, 2.0
+        rng = np.random.default_rng(0)
+        load = rng.pareto(1.5, size=R) + 1.0
+        a = np.maximum(load - load.mean(), 0.0)
+        b = np.maximum(load.mean() - load, 0.0)
+        b *= a.sum() / b.sum()
+        node = np.arange(R) // per_node
+        C = np.where(node[:, None] == node[None, :], 0.0, lam)
+        t = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float64)).to(dev)
+        at, bt, Ct = t(a), t(b), t(C)
+        cfg = {"workload": "sinkhorn_r64", "R": R, "ranks_per_node": per_node, "eps": lam, "iters": 50}
+        call = lambda: lbs.moe_sinkhorn_plan(at, bt, Ct, lam, 50)
+        cpu_call = lambda: __import__("oracle").sinkhorn(a, b, C, lam, 50)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(K):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / K
+    cpu = None
+    if args.cpu_seconds > 0:
+        n, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 2.0) or n == 0:
+            cpu_call()
+            n += 1
+        cpu_us = (time.perf_counter() - t0) / n * 1e6
+        cpu = {"value": cpu_us, "unit": "us per call", "cores": 1, "kind": "oracle",
+               "sample": f"the same call on the host, {n} repetitions"}
+    print(json.dumps({"metric": "planner latency", "value": us, "unit": "us per call", "n_gpus": 1,
+                      "steps": K, "warmup": args.warmup, "ms_per_step": us * 1e-3,
+                      "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+                      "dtype": "int64/f64", "data": "synthetic", "config": cfg,
+                      "roofline": {"bound": "latency", "achieved": None, "peak": None, "unit": None,
+                                   "frac": None, "traffic": None},
+                      "cpu_baseline": cpu}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(this build has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
+    if args.workload in PLANNERS:
+        planner_bench(args)
+        return
 
     import numpy as np
     import torch

@@ -549,6 +549,20 @@ MOE_DEV int wave_min_i(int v) {
     return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
                min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
 }
+MOE_DEV double wave_min_f64(double v) {
+    v = fmin(v, xstep_f64<1>(v));
+    v = fmin(v, xstep_f64<2>(v));
+    v = fmin(v, xstep_f64<4>(v));
+    v = fmin(v, xstep_f64<8>(v));
+    return fmin(fmin(readlane_f64(v, 0), readlane_f64(v, 16)), fmin(readlane_f64(v, 32), readlane_f64(v, 48)));
+}
+MOE_DEV double wave_max_f64(double v) {
+    v = fmax(v, xstep_f64<1>(v));
+    v = fmax(v, xstep_f64<2>(v));
+    v = fmax(v, xstep_f64<4>(v));
+    v = fmax(v, xstep_f64<8>(v));
+    return fmax(fmax(readlane_f64(v, 0), readlane_f64(v, 16)), fmax(readlane_f64(v, 32), readlane_f64(v, 48)));
+}
 // Inclusive prefix sum over the 64 lanes of a wave.
 MOE_DEV int wave_incl_scan_i(int v) { return seg_incl_scan<64>(v, __lane_id()); }
 
