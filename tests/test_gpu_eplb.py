@@ -72,3 +72,17 @@ def test_eplb_on_routing_counts():
     r0 = oracle.eplb(counts[3], w.E, 64)
     r1 = oracle.eplb(counts[3], w.E + 64, 64)
     assert r1["pack_load"].max() < r0["pack_load"].max()
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_eplb_small_integer_loads(seed):
+    """Weights drawn from a handful of small integers: equal per-replica loads
+    and equal pack loads at every step, so runs of placements end on ties and
+    single placements alternate with runs."""
+    rng = np.random.default_rng(100 + seed)
+    E = int(rng.integers(1, 300))
+    packs = int(rng.choice([1, 2, 3, 8, 16, 48, 64, 96]))
+    per = int(np.ceil(E / packs)) + int(rng.integers(0, 4))
+    print(f"case eplb small-int seed={seed} E={E} P={packs * per} packs={packs}", flush=True)
+    w = rng.choice([0, 1, 2, 3, 4, 6, 12], size=E).astype(np.int32)
+    _compare(w, packs * per, packs)
