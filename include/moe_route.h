@@ -252,7 +252,7 @@ int moe_eplb_plan(int32_t E, int32_t num_phys, int32_t num_packs, const int32_t 
                   int32_t *slot, double *pack_load, void *stream);
 
 /*
- * Sinkhorn-Knopp flow plan ([p4] TAOT section 2, Phase 1), one wave:
+ * Sinkhorn-Knopp flow plan ([p4] TAOT section 2, Phase 1), one workgroup:
  * supply a [R] (each rank's overload), demand b [R] (idle capacity; the
  * totals should be equal), cost [R,R] row-major (topology cost between
  * ranks), eps > 0 the entropy regularisation.  Gibbs kernel

@@ -1,7 +1,7 @@
 """Sinkhorn-Knopp flow plan (LoongForge TAOT blog, section 2, Phase 1) on
-the GPU against the CPU oracle.  fp64 on both sides with sums in the same
-order; exp may differ in the last ulp, so T, u, v are compared to 1e-10
-relative."""
+the GPU against the CPU oracle.  fp64 on both sides; the GPU forms each sum
+as four quarter sums of four interleaved partials and exp may differ in the
+last ulp, so T, u, v are compared to 1e-10 relative."""
 import numpy as np
 import pytest
 import torch
