@@ -65,7 +65,9 @@ inline RowCfg choose_rows(int T, int E, int k, int n_micro, bool bias = false) {
     // 12 when it owns 24.
     // The selection-bias variant keeps G more registers per lane: 12 waves
     // when a lane owns up to 16 columns, 8 when it owns 24.
-    c.NW = bias ? ((c.G > 16) ? 8 : 12) : ((c.G > 16) ? 12 : 16);
+    // One or two lanes per row with 16 columns hold more per-row state per
+    // lane (ranking passes): 12 waves there too, so nothing spills.
+    c.NW = bias ? ((c.G > 16) ? 8 : 12) : ((c.G > 16 || (S <= 2 && c.G >= 16)) ? 12 : 16);
     const int W = 64 / S;
     const long per_iter = long(c.NW) * W;
     const long Tm = T / n_micro;
@@ -95,7 +97,10 @@ __host__ __device__ inline void block_rows(int b, int bpm, int Tm, long& begin, 
 
 // Candidate-list capacity per row for the threshold top-k (see route_rows).
 __host__ __device__ constexpr int cand_cap(int S, int G) {
-    return (S * G < (2 * S > 32 ? 2 * S : 32)) ? S * G : (2 * S > 32 ? 2 * S : 32);
+    // narrow segments (k <= 4) keep a 16-entry list: fewer ranking passes in
+    // registers; a longer candidate list takes the exact fallback
+    return (S <= 4) ? ((S * G < 16) ? S * G : 16)
+                    : ((S * G < (2 * S > 32 ? 2 * S : 32)) ? S * G : (2 * S > 32 ? 2 * S : 32));
 }
 
 // Candidate-list row stride (keys): room for the list padded to a multiple of
