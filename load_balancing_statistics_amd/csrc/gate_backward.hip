@@ -5,11 +5,21 @@
 // dlogits is the routing gradient with respect to the logits.
 //
 // Both products stream X (or dX) once and are bound by HBM (about 6 flop per
-// byte), so they run on the vector ALUs, fused in one pass.  A block owns a
+// byte), fused in one pass.  For E <= 16 the reduction over tokens, dWg, runs
+// on the matrix cores (v_mfma_f32_16x16x4_f32, fp32 in and out): 16 lanes
+// share a row, lane n of a row holds CPL consecutive columns, and a step of
+// four rows is, for each of the lane's CPL column offsets q, the product of
+// A = dlogits [16 experts x 4 rows] (lane l: row l/16, expert l%16) and
+// B_q = X [4 rows x 16 columns] (lane l: row l/16, column CPL*(l%16) + q),
+// accumulated in a 16 x 16 tile per q.  dX stays on the vector ALUs: each
+// lane takes its row's E gradients from lanes 16*(l/16) + e (DPP row
+// broadcast) and forms its CPL outputs, rounded to bf16 in hardware.
+//
+// For 16 < E <= 64 both products run on the vector ALUs.  A block owns a
 // 64-column tile of X over a contiguous slice of the tokens; a lane owns CPL
-// consecutive columns of one row per step (CPL = 8, 4, 2, 1 for E <= 8, 16,
-// 32, 64, keeping CPL*E <= 64 fp32 accumulators), so a row's 64 columns are
-// 128 contiguous bytes.  Per row the lane reads its X chunk and the row's E
+// consecutive columns of one row per step (CPL = 2, 1 for E <= 32, 64,
+// keeping CPL*E <= 64 fp32 accumulators), so a row's 64 columns are 128
+// contiguous bytes.  Per row the lane reads its X chunk and the row's E
 // gradients, writes its dX chunk (its CPL x E slice of Wg stays in registers)
 // and adds X * dlogits into its dWg accumulators.  The accumulators are
 // reduced over the lanes and waves of the block in a fixed order into a
@@ -157,6 +167,129 @@ gate_backward_kernel(const GateBackArgs a)
     }
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+constexpr int kMfWaves = 4;
+constexpr int kMfRowSteps = 8;  // 4-row steps whose loads are issued together
+
+template <int CTRL>
+__device__ __forceinline__ float row_bcast(float v) {  // lane CTRL - 0x150 of the 16-lane row
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// EM: experts padded (8 or 16); CPL: columns per lane (tile = 16 * CPL).
+template <int EM, int CPL>
+__global__ void __launch_bounds__(kMfWaves * 64)
+gate_backward_mfma_kernel(const GateBackArgs a)
+{
+    constexpr int kTileM = 16 * CPL;
+    const int E = a.E, d = a.d;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15, r = lane >> 4;  // column group, row of the 4-row step
+    const int col0 = blockIdx.x * kTileM + CPL * n;
+    const bool col_ok = col0 < d;            // d % 8 == 0: a lane's columns are all in or all out
+    const long t0 = (long(blockIdx.y) * a.T) / gridDim.y;
+    const long t1 = (long(blockIdx.y + 1) * a.T) / gridDim.y;
+
+    float wg[CPL][EM];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c)
+#pragma unroll
+        for (int e = 0; e < EM; ++e)
+            wg[c][e] = (col_ok && e < E) ? bf16_to_f32(a.Wg[long(col0 + c) * E + e]) : 0.f;
+    f32x4 acc[CPL];
+#pragma unroll
+    for (int q = 0; q < CPL; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const long step = 4L * kMfWaves;
+    for (long s0 = t0 + 4L * wave; s0 < t1; s0 += step * kMfRowSteps) {
+        uint32_t xv[kMfRowSteps][CPL / 2];
+        float dv[kMfRowSteps];
+#pragma unroll
+        for (int u = 0; u < kMfRowSteps; ++u) {
+            const long row = s0 + u * step + r;
+            const bool in = row < t1;
+            const long rr = in ? row : t0;
+            if constexpr (CPL == 8) {
+                const uint4 v = col_ok ? *reinterpret_cast<const uint4*>(a.X + rr * d + col0) : make_uint4(0, 0, 0, 0);
+                xv[u][0] = v.x; xv[u][1] = v.y; xv[u][2] = v.z; xv[u][3] = v.w;
+            } else {
+                const uint2 v = col_ok ? *reinterpret_cast<const uint2*>(a.X + rr * d + col0) : make_uint2(0, 0);
+                xv[u][0] = v.x; xv[u][1] = v.y;
+            }
+            const float g = (n < E) ? a.dlogits[rr * E + n] : 0.f;
+            dv[u] = in ? g : 0.f;  // rows past the slice add nothing to dWg
+        }
+#pragma unroll
+        for (int u = 0; u < kMfRowSteps; ++u) {
+            const long row = s0 + u * step + r;
+            float x[CPL];
+#pragma unroll
+            for (int h = 0; h < CPL / 2; ++h) {
+                x[2 * h] = bf16_to_f32(uint16_t(xv[u][h]));
+                x[2 * h + 1] = bf16_to_f32(uint16_t(xv[u][h] >> 16));
+            }
+#pragma unroll
+            for (int q = 0; q < CPL; ++q) acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(dv[u], x[q], acc[q], 0, 0, 0);
+            if (a.dX) {
+                // the broadcasts read lanes 16*(l/16) + e, which must be active:
+                // taken by the whole wave, before the per-lane bounds
+                float g[EM];
+                g[0] = row_bcast<0x150>(dv[u]); g[1] = row_bcast<0x151>(dv[u]);
+                g[2] = row_bcast<0x152>(dv[u]); g[3] = row_bcast<0x153>(dv[u]);
+                g[4] = row_bcast<0x154>(dv[u]); g[5] = row_bcast<0x155>(dv[u]);
+                g[6] = row_bcast<0x156>(dv[u]); g[7] = row_bcast<0x157>(dv[u]);
+                if constexpr (EM == 16) {
+                    g[8 % EM] = row_bcast<0x158>(dv[u]); g[9 % EM] = row_bcast<0x159>(dv[u]);
+                    g[10 % EM] = row_bcast<0x15A>(dv[u]); g[11 % EM] = row_bcast<0x15B>(dv[u]);
+                    g[12 % EM] = row_bcast<0x15C>(dv[u]); g[13 % EM] = row_bcast<0x15D>(dv[u]);
+                    g[14 % EM] = row_bcast<0x15E>(dv[u]); g[15 % EM] = row_bcast<0x15F>(dv[u]);
+                }
+                if (col_ok && row < t1) {
+                    uint32_t pk[CPL / 2];
+#pragma unroll
+                    for (int h = 0; h < CPL / 2; ++h) {
+                        float o0 = 0.f, o1 = 0.f;
+#pragma unroll
+                        for (int e = 0; e < EM; ++e) {
+                            o0 = fmaf(g[e], wg[2 * h][e], o0);
+                            o1 = fmaf(g[e], wg[2 * h + 1][e], o1);
+                        }
+                        pk[h] = uint32_t(__builtin_bit_cast(uint16_t, (__bf16)o0)) |
+                                (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)o1)) << 16);
+                    }
+                    if constexpr (CPL == 8)
+                        *reinterpret_cast<uint4*>(a.dX + row * d + col0) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+                    else
+                        *reinterpret_cast<uint2*>(a.dX + row * d + col0) = make_uint2(pk[0], pk[1]);
+                }
+            }
+        }
+    }
+
+    if (!a.dWg_part) return;
+    // tile q, element i of lane l: column CPL*(l%16) + q of the block, expert
+    // 4*(l/16) + i; waves combined in order through LDS
+    __shared__ float wred[kTileM][16];
+    for (int w = 0; w < kMfWaves; ++w) {
+        if (wave == w) {
+#pragma unroll
+            for (int q = 0; q < CPL; ++q)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float& slot = wred[CPL * n + q][4 * r + i];
+                    slot = (w == 0) ? acc[q][i] : slot + acc[q][i];
+                }
+        }
+        __syncthreads();
+    }
+    float* part = a.dWg_part + long(blockIdx.y) * d * E;
+    for (int i = threadIdx.x; i < kTileM * E; i += kMfWaves * 64) {
+        const int cc = i / E, e = i - (i / E) * E;
+        const int col = blockIdx.x * kTileM + cc;
+        if (col < d) part[long(col) * E + e] = wred[cc][e];
+    }
+}
+
 // dWg[i] = sum over the token slices of part[slice][i], slices in order.
 __global__ void __launch_bounds__(256)
 gate_backward_reduce_kernel(const float* __restrict__ part, float* __restrict__ dWg, long n, int slices)
@@ -170,9 +303,13 @@ gate_backward_reduce_kernel(const float* __restrict__ part, float* __restrict__ 
 
 }  // namespace
 
+// Columns per block of the kernel that serves E.
+static int gate_backward_tile(int E) { return E <= 8 ? 128 : kTile; }
+
 // Token slices: enough blocks for two per compute unit, at least 64 rows each.
-int gate_backward_slices(int T, int d) {
-    const long tiles = (d + kTile - 1) / kTile;
+int gate_backward_slices(int T, int d, int E) {
+    const int tile = gate_backward_tile(E);
+    const long tiles = (d + tile - 1) / tile;
     long sl = (2L * kAssumedCUs + tiles - 1) / tiles;
     const long max_sl = (T + 63) / 64;
     if (sl > max_sl) sl = max_sl;
@@ -181,16 +318,17 @@ int gate_backward_slices(int T, int d) {
 }
 
 size_t gate_backward_workspace_bytes(int T, int d, int E) {
-    return align_up(size_t(gate_backward_slices(T, d)) * d * E * 4, 256);
+    return align_up(size_t(gate_backward_slices(T, d, E)) * d * E * 4, 256);
 }
 
 hipError_t launch_gate_backward(const GateBackArgs& a, hipStream_t st) {
-    const int slices = gate_backward_slices(a.T, a.d);
-    const dim3 grid((a.d + kTile - 1) / kTile, slices);
+    const int slices = gate_backward_slices(a.T, a.d, a.E);
+    const int tile = gate_backward_tile(a.E);
+    const dim3 grid((a.d + tile - 1) / tile, slices);
     GateBackArgs b = a;
     if (!a.dWg) b.dWg_part = nullptr;
-    if (a.E <= 8) hipLaunchKernelGGL(gate_backward_kernel<8>, grid, dim3(kGbThreads), 0, st, b);
-    else if (a.E <= 16) hipLaunchKernelGGL(gate_backward_kernel<4>, grid, dim3(kGbThreads), 0, st, b);
+    if (a.E <= 8) hipLaunchKernelGGL((gate_backward_mfma_kernel<8, 8>), grid, dim3(kMfWaves * 64), 0, st, b);
+    else if (a.E <= 16) hipLaunchKernelGGL((gate_backward_mfma_kernel<16, 4>), grid, dim3(kMfWaves * 64), 0, st, b);
     else if (a.E <= 32) hipLaunchKernelGGL(gate_backward_kernel<2>, grid, dim3(kGbThreads), 0, st, b);
     else if (a.E <= 64) hipLaunchKernelGGL(gate_backward_kernel<1>, grid, dim3(kGbThreads), 0, st, b);
     else return hipErrorInvalidValue;

@@ -322,7 +322,7 @@ hipError_t launch_gate_backward(const GateBackArgs& a, hipStream_t st);
 hipError_t launch_eplb(const EplbArgs& a, hipStream_t st);
 hipError_t launch_sinkhorn(const SinkhornArgs& a, hipStream_t st);
 size_t eplb_lds_bytes(int E, int num_phys);
-int gate_backward_slices(int T, int d);
+int gate_backward_slices(int T, int d, int E);
 size_t gate_backward_workspace_bytes(int T, int d, int E);
 hipError_t launch_gate_gemm(const GateArgs& a, uint16_t* wt, hipStream_t st);
 bool gate_supported(int T, int d, int E);

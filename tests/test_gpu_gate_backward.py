@@ -52,7 +52,7 @@ def _check(T, d, E, X, W, G, got_dx, got_dw):
 
 
 @pytest.mark.parametrize("shape", [(1000 + 7, 256, 8), (777, 128, 16), (300, 64, 33), (129, 72, 64),
-                                   (5, 8, 1), (4096, 520, 3)],
+                                   (5, 8, 1), (4096, 520, 3), (2000, 200, 12), (64, 1024, 8)],
                          ids=lambda s: "T%d_d%d_E%d" % s)
 def test_gate_backward_small(shape):
     T, d, E = shape
