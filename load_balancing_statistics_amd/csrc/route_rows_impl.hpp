@@ -55,6 +55,56 @@ __device__ __forceinline__ int count_ge(float lmax) {
     }
 }
 
+// Order-preserving integer key of a float (monotone for non-NaN values,
+// -0.0 just below +0.0) and its inverse: integer max/min need no NaN
+// canonicalisation and fuse with the DPP move of their operand.
+__device__ __forceinline__ int order_key(float f) {
+    const int b = __float_as_int(f);
+    return b ^ ((b >> 31) & 0x7FFFFFFF);
+}
+__device__ __forceinline__ float from_order_key(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF)); }
+
+// One compare-exchange: lanes set in keep (a fixed pattern of the wave, held
+// in a scalar mask) keep the larger of (v, partner), the others the smaller.
+__device__ __forceinline__ int cx_keep(int v, int p, uint64_t keep) {
+    const int mx = max(v, p), mn = min(v, p);
+    return __builtin_amdgcn_inverse_ballot_w64(keep) ? mx : mn;
+}
+
+// Bitonic sort, descending, of one value per lane within each 16-lane row:
+// merges of 2, 4, 8, 16 lanes, each opened by a mirror compare (the lower
+// half keeps the larger) and closed by half-cleaners at distances 4, 2, 1.
+__device__ __forceinline__ int sort16_desc(int v) {
+    constexpr uint64_t kEven = 0x5555555555555555ull;  // (i & 1) == 0
+    constexpr uint64_t kLow2 = 0x3333333333333333ull;  // (i & 2) == 0
+    constexpr uint64_t kLow4 = 0x0F0F0F0F0F0F0F0Full;  // (i & 4) == 0
+    constexpr uint64_t kLow8 = 0x00FF00FF00FF00FFull;  // (i & 8) == 0
+    v = cx_keep(v, dppi<0xB1>(v), kEven);    // 2: lane i <-> i^1
+    v = cx_keep(v, dppi<0x1B>(v), kLow2);    // 4: quad_perm [3,2,1,0], mirror
+    v = cx_keep(v, dppi<0xB1>(v), kEven);
+    v = cx_keep(v, dppi<0x141>(v), kLow4);   // 8: row_half_mirror
+    v = cx_keep(v, dppi<0x4E>(v), kLow2);    //    i^2
+    v = cx_keep(v, dppi<0xB1>(v), kEven);    //    i^1
+    v = cx_keep(v, dppi<0x140>(v), kLow8);   // 16: row_mirror
+    {
+        // i^4: lane i reads i + 4 (row_ror:12) or i - 4 (row_ror:4)
+        const int up = dppi<0x12C>(v), dn = dppi<0x124>(v);
+        v = cx_keep(v, __builtin_amdgcn_inverse_ballot_w64(kLow4) ? up : dn, kLow4);
+    }
+    v = cx_keep(v, dppi<0x4E>(v), kLow2);    //    i^2
+    v = cx_keep(v, dppi<0xB1>(v), kEven);    //    i^1
+    return v;
+}
+
+// Minimum over each 16-lane row.
+__device__ __forceinline__ int seg16_min(int v) {
+    v = min(v, dppi<0xB1>(v));
+    v = min(v, dppi<0x4E>(v));
+    v = min(v, dppi<0x141>(v));
+    v = min(v, dppi<0x140>(v));
+    return v;
+}
+
 template <int S, int VEC>
 __device__ __forceinline__ int col_of(int g, int s) {
     return VEC * ((g / VEC) * S + s) + (g % VEC);
@@ -150,19 +200,28 @@ struct RowPass {
         float lmax = x[0];
 #pragma unroll
         for (int g = 1; g < G; ++g) lmax = fmaxf(lmax, x[g]);
-        const float m = seg_max<S>(lmax);
         float ymax = lmax;
         if constexpr (BIAS) {
             ymax = x[0] + bz[0];
 #pragma unroll
             for (int g = 1; g < G; ++g) ymax = fmaxf(ymax, x[g] + bz[g]);
         }
-        float tau = BIAS ? seg_max<S>(ymax) : m;
-        if constexpr (S > 1) {
-            if (k > 1) {
-                const int ge = count_ge<S, 1>(ymax);
-                // the largest lane maximum reached by at least k lane maxima
-                tau = seg_max<S>(ge >= k ? ymax : -INFINITY);
+        float m, tau;
+        if constexpr (S == 16) {
+            // the segment's lane maxima sorted (descending) across its 16
+            // lanes: tau is the k-th, and without a bias m is the first
+            const int sk = sort16_desc(order_key(ymax));
+            tau = from_order_key(seg16_min((s < k) ? sk : 0x7FFFFFFF));
+            m = BIAS ? seg_max<S>(lmax) : from_order_key(dppi<0x150>(sk));  // row_newbcast:0
+        } else {
+            m = seg_max<S>(lmax);
+            tau = BIAS ? seg_max<S>(ymax) : m;
+            if constexpr (S > 1) {
+                if (k > 1) {
+                    const int ge = count_ge<S, 1>(ymax);
+                    // the largest lane maximum reached by at least k lane maxima
+                    tau = seg_max<S>(ge >= k ? ymax : -INFINITY);
+                }
             }
         }
 
