@@ -207,9 +207,11 @@ struct RowPass {
             for (int g = 1; g < G; ++g) ymax = fmaxf(ymax, x[g] + bz[g]);
         }
         float m, tau;
-        if constexpr (S == 16) {
+        if constexpr (S == 16 && G <= 16) {
             // the segment's lane maxima sorted (descending) across its 16
             // lanes: tau is the k-th, and without a bias m is the first
+            // (24-column lanes keep the rank count: the sort's temporaries
+            // would push them past the 12-wave register budget)
             const int sk = sort16_desc(order_key(ymax));
             tau = from_order_key(seg16_min((s < k) ? sk : 0x7FFFFFFF));
             m = BIAS ? seg_max<S>(lmax) : from_order_key(dppi<0x150>(sk));  // row_newbcast:0
