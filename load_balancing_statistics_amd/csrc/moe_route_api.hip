@@ -181,6 +181,7 @@ int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
     ca.T = p->T; ca.E = p->E; ca.k = p->k; ca.Tm = Tm; ca.bpm = c.bpm; ca.nsplit = c.nsplit;
     ca.rows_per_wave = moe::scatter_rows_per_wave(p->E, p->k);
     ca.capacity = int(capacity_of(p));
+    ca.vec_idx = (p->k % 4 == 0 && aligned(out->topk_idx, 16)) ? 1 : 0;
     ca.perm = out->perm;
     ca.inv_perm = (p->flags & MOE_WRITE_INV_PERM) ? out->inv_perm : nullptr;
     ca.dropped = out->dropped; ca.status = out->status;

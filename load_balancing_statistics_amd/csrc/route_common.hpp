@@ -227,6 +227,7 @@ struct ScatterArgs {
     int T, E, k, Tm, bpm, nsplit;
     int rows_per_wave;  // rows a wave ranks per window (<= 64, one mask bit each)
     int capacity;  // < 0: unlimited
+    int vec_idx;   // topk_idx 16-byte aligned and k % 4 == 0: vector index loads
     int32_t* perm;
     int32_t* inv_perm;
     uint8_t* dropped;

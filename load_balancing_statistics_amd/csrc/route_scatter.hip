@@ -12,7 +12,10 @@
 // A token picks an expert at most once (its top-k are distinct), so inside an
 // expert the (t, j) order is the token order.  The block walks its rows in
 // windows; in a window each wave owns a contiguous run of rows, row r of the
-// run being bit r of a 64-bit mask per (wave, expert).  Every slot (r, j)
+// run being bit r of a 64-bit mask per (wave, expert).  The lanes of a row
+// hold contiguous chunks of its k slots, read as 16-byte vectors when the
+// chunks are whole vectors (every load instruction then covers contiguous
+// bytes).  Every slot (r, j)
 // ORs its bit into the mask of its expert; a slot's rank among the wave's
 // assignments to that expert is then the popcount of the mask below its bit,
 // and the wave's count is the whole popcount.  An exclusive scan over the
@@ -74,16 +77,17 @@ __device__ __forceinline__ int logical_block() {
 // never exceeds KM.
 constexpr int KM = 8;
 
-__global__ void __launch_bounds__(kScatMaxWaves * 64)
+// NW waves per block (the launch uses exactly NW * 64 threads).
+template <int NW>
+__global__ void __launch_bounds__(NW * 64)
 route_scatter_kernel(const ScatterArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     const int E = a.E, k = a.k;
-    const int NW = int(blockDim.x) >> 6;
     const int E4 = (E + 1 + 3) & ~3;
     uint64_t* gm = reinterpret_cast<uint64_t*>(smem);      // [NW][E] row masks
-    int2* rec = reinterpret_cast<int2*>(gm + NW * E);       // [NW][E] {window place, segment place} of the wave's first
-    int2* st = rec + NW * E;                                // [stage] {assignment, segment place}, expert order
+    int* wpre = reinterpret_cast<int*>(gm + NW * E);        // [NW][E] e's assignments in the earlier waves
+    int2* st = reinterpret_cast<int2*>(wpre + NW * E);      // [stage] {assignment, segment place}, expert order
     int* base = reinterpret_cast<int*>(st + NW * a.rows_per_wave * k);  // [E] the block's next place for e
     int* lim = base + E4;                                   // [E] first dropped place of e
     int* tot = lim + E4;                                    // [E4] window counts
@@ -100,10 +104,11 @@ route_scatter_kernel(const ScatterArgs a)
     const long seglen = long(a.Tm) * k;
     const int WR = NW * a.rows_per_wave;       // rows per window
 
-    // slot layout of a window: rows per wave, lanes per row
+    // slot layout of a window: rows per wave, lanes per row, and lane g of a
+    // row holds slots j = g*KC + u, u < KC
     int ev[KM];
     long row = 0;
-    int rl = 0, g = 0, lpr = 1;
+    int rl = 0, g = 0, KC = 1;
     bool active = false;
     auto load_window = [&](long w0) {
         const long w1 = min(w0 + long(WR), row_end);
@@ -111,15 +116,28 @@ route_scatter_kernel(const ScatterArgs a)
         const int rpw = (nrows + NW - 1) / NW;
         int rp = 1;
         while (rp < rpw) rp <<= 1;
-        lpr = 64 / rp;
+        const int lpr = 64 / rp;
+        KC = (k + lpr - 1) / lpr;
         rl = lane & (rp - 1);
         g = lane / rp;
         row = w0 + long(wave) * rpw + rl;
         active = rl < rpw && row < w1;
+        const long i0 = row * k + long(g) * KC;
+        if (a.vec_idx && (KC & 3) == 0) {
+            // k and KC multiples of 4: a lane's chunk is KC/4 aligned vectors
 #pragma unroll
-        for (int u = 0; u < KM; ++u) {
-            const int j = g + u * lpr;
-            ev[u] = load_or(a.topk_idx, row * k + j, active && j < k, -1);
+            for (int q = 0; q < KM / 4; ++q) {
+                const bool in = active && 4 * q < KC && g * KC + 4 * q < k;
+                const int4 v = *reinterpret_cast<const int4*>(a.topk_idx + (in ? i0 + 4 * q : 0));
+                ev[4 * q] = in ? v.x : -1;
+                ev[4 * q + 1] = in ? v.y : -1;
+                ev[4 * q + 2] = in ? v.z : -1;
+                ev[4 * q + 3] = in ? v.w : -1;
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < KM; ++u)
+                ev[u] = load_or(a.topk_idx, i0 + u, active && u < KC && g * KC + u < k, -1);
         }
     };
     load_window(row_begin);
@@ -141,7 +159,7 @@ route_scatter_kernel(const ScatterArgs a)
     }
 
     uint64_t* mym = gm + wave * E;
-    const int2* myrec = rec + wave * E;
+    const int* mypre = wpre + wave * E;
     int internal = 0;
     for (long w0 = row_begin; w0 < row_end; w0 += WR) {
         if (w0 != row_begin) load_window(w0);
@@ -154,37 +172,26 @@ route_scatter_kernel(const ScatterArgs a)
         for (int u = 0; u < KM; ++u) {
             const int e = ev[u];
             if (e >= 0 && e < E) atomicOr(reinterpret_cast<unsigned long long*>(&mym[e]), bit);
-            else if (active && g + u * lpr < k) internal = 1;
+            else if (active && u < KC && g * KC + u < k) internal = 1;
         }
         __syncthreads();
-        // window count of every expert
-        for (int e = tid; e < E; e += blockDim.x) {
-            int c[kScatMaxWaves];
+        // window count of every expert, and per wave the count in the
+        // earlier waves
+        for (int e = tid; e < E; e += NW * 64) {
+            int c[NW];
 #pragma unroll
-            for (int w = 0; w < kScatMaxWaves; ++w) c[w] = (w < NW) ? __popcll(gm[w * E + e]) : 0;
+            for (int w = 0; w < NW; ++w) c[w] = __popcll(gm[w * E + e]);
             int t = 0;
 #pragma unroll
-            for (int w = 0; w < kScatMaxWaves; ++w) t += c[w];
+            for (int w = 0; w < NW; ++w) {
+                wpre[w * E + e] = t;
+                t += c[w];
+            }
             tot[e] = t;
         }
         __syncthreads();
-        block_excl_scan(tot, E, lofs, wsum);
+        block_excl_scan(tot, E, lofs, wsum);  // ends with a barrier
         const int nvalid = lofs[E];
-        // per (wave, expert): where the wave's first assignment to e goes,
-        // inside the window and inside the segment
-        for (int e = tid; e < E; e += blockDim.x) {
-            int c[kScatMaxWaves];
-#pragma unroll
-            for (int w = 0; w < kScatMaxWaves; ++w) c[w] = (w < NW) ? __popcll(gm[w * E + e]) : 0;
-            int lp = lofs[e], sp = base[e];
-#pragma unroll
-            for (int w = 0; w < kScatMaxWaves; ++w) {
-                if (w < NW) rec[w * E + e] = make_int2(lp, sp);
-                lp += c[w];
-                sp += c[w];
-            }
-        }
-        __syncthreads();
 
         // every slot: rank among the wave's assignments to its expert, places
         const uint64_t below = bit - 1;
@@ -193,11 +200,10 @@ route_scatter_kernel(const ScatterArgs a)
         for (int u = 0; u < KM; ++u) {
             const int e = ev[u];
             if (e < 0 || e >= E) continue;
-            const int j = g + u * lpr;
-            const int rank = __popcll(mym[e] & below);
-            const int2 r = myrec[e];
-            const int lp = r.x + rank;
-            const long pos = long(r.y) + rank;
+            const int j = g * KC + u;
+            const int rank = __popcll(mym[e] & below) + mypre[e];
+            const int lp = lofs[e] + rank;          // place in the window
+            const long pos = long(base[e]) + rank;  // place in the segment
             const long i = ibase + j;
             const bool in_seg = pos >= 0 && pos < seglen;
             if (lp < 0 || lp >= nvalid || !in_seg) internal = 1;
@@ -230,7 +236,7 @@ int rows_cap_for_k(int k) {
 size_t lds_for(int E, int NW, int rpw, int k) {
     const size_t E4 = size_t((E + 1 + 3) & ~3);
     const size_t stage = size_t(NW) * rpw * k;
-    return size_t(NW) * E * 16 + stage * 8 + 4 * E4 * 4;
+    return size_t(NW) * E * 12 + stage * 8 + 4 * E4 * 4;
 }
 
 }  // namespace
@@ -248,19 +254,24 @@ size_t scatter_lds_bytes(int E, int k) {
     return lds_for(E, scatter_waves(E), scatter_rows_per_wave(E, k), k);
 }
 
+template <int NW>
+hipError_t launch_scatter_nw(const RowCfg& c, const ScatterArgs& a, size_t lds, hipStream_t st) {
+    if (lds > 64 * 1024) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(route_scatter_kernel<NW>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(route_scatter_kernel<NW>, dim3(c.B), dim3(NW * 64), lds, st, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_route_scatter(const RowCfg& c, const ScatterArgs& a, hipStream_t st) {
     const int NW = scatter_waves(a.E);
     const size_t lds = lds_for(a.E, NW, a.rows_per_wave, a.k);
     if (a.k > MOE_ROUTE_MAX_K || a.E > MOE_ROUTE_MAX_E || a.rows_per_wave < 1 ||
         a.rows_per_wave > rows_cap_for_k(a.k))
         return hipErrorInvalidValue;
-    if (lds > 64 * 1024) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(route_scatter_kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(route_scatter_kernel, dim3(c.B), dim3(NW * 64), lds, st, a);
-    return hipGetLastError();
+    return NW == 16 ? launch_scatter_nw<16>(c, a, lds, st) : launch_scatter_nw<8>(c, a, lds, st);
 }
 
 }  // namespace moe
