@@ -155,7 +155,6 @@ int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
     ra.qcap = moe::rows_queue_cap(c);
     ra.topk_idx = out->topk_idx; ra.topk_w = out->topk_w; ra.row_stats = out->row_stats;
     ra.cnt_part = ws.cnt_part; ra.P_part = ws.P_part; ra.flag_part = ws.flag_part;
-    ra.arrive = ws.arrive; ra.n_micro = p->n_micro;
     const bool timed = out->row_pass_events[0] && out->row_pass_events[1];
     if (timed && hipEventRecord(static_cast<hipEvent_t>(out->row_pass_events[0]), st) != hipSuccess)
         return MOE_ERR_HIP;
@@ -166,18 +165,19 @@ int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
     moe::ScanArgs sa{};
     sa.cnt_part = ws.cnt_part; sa.P_part = ws.P_part; sa.flag_part = ws.flag_part;
     sa.E = p->E; sa.k = p->k; sa.Tm = Tm; sa.bpm = c.bpm; sa.n_micro = p->n_micro; sa.B = c.B;
-    sa.nsplit = c.nsplit; sa.capacity = int(capacity_of(p)); sa.alpha = p->alpha;
-    sa.p_masked = (p->flags & MOE_P_MASKED) ? 1 : 0;
+    sa.nsplit = c.nsplit;
     sa.colprefix = ws.colprefix; sa.split_tot = ws.split_tot; sa.split_P = ws.split_P;
-    sa.arrive = ws.arrive; sa.status = out->status;
-    sa.counts = out->counts; sa.offsets = out->offsets; sa.f = out->f; sa.P = out->P;
-    sa.aux = out->aux_loss; sa.cv = out->cv; sa.max_over_mean = out->max_over_mean;
-    sa.extra = out->extra_stats;
+    sa.status = out->status;
     if (moe::launch_route_scan(c, sa, st) != hipSuccess) return MOE_ERR_HIP;
 
     moe::ScatterArgs ca{};
     ca.topk_idx = out->topk_idx; ca.colprefix = ws.colprefix; ca.split_tot = ws.split_tot;
-    ca.offsets = out->offsets;
+    ca.split_P = ws.split_P;
+    ca.alpha = p->alpha;
+    ca.p_masked = (p->flags & MOE_P_MASKED) ? 1 : 0;
+    ca.counts = out->counts; ca.offsets = out->offsets; ca.f = out->f; ca.P = out->P;
+    ca.aux = out->aux_loss; ca.cv = out->cv; ca.max_over_mean = out->max_over_mean;
+    ca.extra = out->extra_stats;
     ca.T = p->T; ca.E = p->E; ca.k = p->k; ca.Tm = Tm; ca.bpm = c.bpm; ca.nsplit = c.nsplit;
     ca.rows_per_wave = moe::scatter_rows_per_wave(p->E, p->k);
     ca.capacity = int(capacity_of(p));

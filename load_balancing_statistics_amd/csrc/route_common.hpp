@@ -140,7 +140,6 @@ struct Workspace {
     int32_t* colprefix;   // [B,E]        exclusive prefix over the blocks of a split
     int32_t* split_tot;   // [m,nsplit,E] counts per split
     double*  split_P;     // [m,nsplit,E] probability sums per split
-    int32_t* arrive;      // [m]          scan blocks finished per microbatch
     uint16_t* Wt;         // [E,d]        transposed gate weights (gate path only)
     size_t   bytes;
 };
@@ -160,7 +159,6 @@ inline Workspace carve_workspace(void* base, const RowCfg& c, int E, int m, size
     size_t o_pre = take(B * E * 4);
     size_t o_tot = take(size_t(m) * ns * E * 4);
     size_t o_ps = take(size_t(m) * ns * E * 8);
-    size_t o_arr = take(size_t(m) * 4);
     size_t o_wt = take(gate_bytes);
     w.bytes = off;
     char* b = static_cast<char*>(base);
@@ -171,7 +169,6 @@ inline Workspace carve_workspace(void* base, const RowCfg& c, int E, int m, size
         w.colprefix = reinterpret_cast<int32_t*>(b + o_pre);
         w.split_tot = reinterpret_cast<int32_t*>(b + o_tot);
         w.split_P = reinterpret_cast<double*>(b + o_ps);
-        w.arrive = reinterpret_cast<int32_t*>(b + o_arr);
         w.Wt = gate_bytes ? reinterpret_cast<uint16_t*>(b + o_wt) : nullptr;
     }
     return w;
@@ -191,8 +188,6 @@ struct RowsArgs {
     int32_t* cnt_part;
     float* P_part;
     int32_t* flag_part;
-    int32_t* arrive;  // [n_micro] zeroed by block 0 for the scan that follows
-    int n_micro;
 };
 
 struct ScanArgs {
@@ -200,15 +195,28 @@ struct ScanArgs {
     const float* P_part;
     const int32_t* flag_part;
     int E, k, Tm, bpm, n_micro, B, nsplit;
-    int capacity;  // < 0: unlimited
-    float alpha;
-    int p_masked;  // P_e = probability sum / (Tm*k) instead of / Tm
     int32_t* colprefix;
     int32_t* split_tot;
     double* split_P;
-    int32_t* arrive;
     int32_t* status;
-    // per-microbatch statistics, written by the last scan block of each
+};
+
+struct ScatterArgs {
+    const int32_t* topk_idx;
+    const int32_t* colprefix;
+    const int32_t* split_tot;
+    const double* split_P;
+    int T, E, k, Tm, bpm, nsplit;
+    int rows_per_wave;  // rows a wave ranks per window (<= 64, one mask bit each)
+    int capacity;  // < 0: unlimited
+    int vec_idx;   // topk_idx 16-byte aligned and k % 4 == 0: vector index loads
+    float alpha;
+    int p_masked;  // P_e = probability sum / (Tm*k) instead of / Tm
+    int32_t* perm;
+    int32_t* inv_perm;
+    uint8_t* dropped;
+    int32_t* status;
+    // per-microbatch results, written by the first block of each microbatch
     int32_t* counts;
     int32_t* offsets;
     float* f;
@@ -217,21 +225,6 @@ struct ScanArgs {
     float* cv;
     float* max_over_mean;
     float* extra;
-};
-
-struct ScatterArgs {
-    const int32_t* topk_idx;
-    const int32_t* colprefix;
-    const int32_t* split_tot;
-    const int32_t* offsets;
-    int T, E, k, Tm, bpm, nsplit;
-    int rows_per_wave;  // rows a wave ranks per window (<= 64, one mask bit each)
-    int capacity;  // < 0: unlimited
-    int vec_idx;   // topk_idx 16-byte aligned and k % 4 == 0: vector index loads
-    int32_t* perm;
-    int32_t* inv_perm;
-    uint8_t* dropped;
-    int32_t* status;
 };
 
 struct BackArgs {

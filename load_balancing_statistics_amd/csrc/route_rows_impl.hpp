@@ -441,8 +441,6 @@ route_rows_kernel(const RowsArgs a)
         for (int e = tid; e < E; e += NW * 64) blds[e] = a.bias[e];
     if (a.p_masked)
         for (int e = tid; e < E; e += NW * 64) pm[e] = 0ull;
-    if (blockIdx.x == 0)
-        for (int m = tid; m < a.n_micro; m += NW * 64) a.arrive[m] = 0;
     __syncthreads();
 
     float* rowbuf = rowbuf_all + (wave * W + seg) * RS;

@@ -7,7 +7,11 @@
 // are dropped).  Block b handles the same rows as row block b; its
 // assignments to expert e start at
 //   offsets[e] + (count of e in the earlier splits) + (count of e in the
-//   earlier blocks of its split).
+//   earlier blocks of its split),
+// offsets being the exclusive prefix sum, in expert order, of the
+// microbatch's counts (the sums of its split counts), which every block
+// forms for itself.  The first block of each microbatch also writes the
+// counts, the offsets and the balance statistics.
 //
 // A token picks an expert at most once (its top-k are distinct), so inside an
 // expert the (t, j) order is the token order.  The block walks its rows in
@@ -24,6 +28,8 @@
 // the block's assignments to one expert land in consecutive words, so the
 // stores coalesce.  dropped and inv_perm are indexed by the assignment and
 // are stored from the ranking pass.
+#include <climits>
+
 #include "route_common.hpp"
 
 namespace moe {
@@ -33,6 +39,102 @@ using namespace dev;
 
 constexpr int kScatMaxWaves = 16;
 constexpr int kSplitBatch = 8;
+
+// Counts, offsets and balance statistics of microbatch mb, by one block of
+// NW waves, from the counts tot[0..E) and their exclusive prefix lofs[0..E]
+// (both in LDS), in fp64 with every sum in a fixed order:
+//   f_e = counts_e/(Tm*k) and P_e = probability sum/Tm (or /(Tm*k) for the
+//   masked form of mhpq.cn section 4.4, whose sums cover the picks only) with
+//   aux = alpha*E*sum_e f_e*P_e (mhpq.cn sections 4.2, 4.4; codechina.net
+//   article 413310 section 2.2), CV = population std/mean and balance degree
+//   1-(max-mean)/mean (page cnvsn.com/news/335486 sections 3.1, 5.1),
+//   max/mean load (mhpq.cn section 5.4), entropy and max/min share of f
+//   (codechina.net section 4.2), kept and dropped assignments under C.
+// Every thread forms the terms of its experts (psum[it]: the probability sum
+// of expert tid + it*NW*64 over the splits) into q, four arrays of E doubles
+// in LDS; then waves 0..5 each reduce one quantity (lane-strided sums in
+// expert order, then the lanes) and write its results.  q is free LDS
+// scratch of the caller; the function ends with a barrier.
+template <int NW, int EPT>
+__device__ void microbatch_statistics(const ScatterArgs& a, int mb, const int* tot, const int* lofs,
+                                      const double* psum, double* q) {
+    static_assert(NW >= 6, "one wave per reduced quantity");
+    const int E = a.E;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const double total = double(a.Tm) * double(a.k);
+    const double mean = total / double(E);
+    const long cb = long(mb) * E;
+    // f and P scale by reciprocals formed once (within an ulp of dividing)
+    const double inv_total = 1.0 / total;
+    const double inv_pden = a.p_masked ? inv_total : 1.0 / double(a.Tm);
+#pragma unroll
+    for (int it = 0; it < EPT; ++it) {
+        const int e = tid + it * NW * 64;
+        if (e >= E) break;
+        const int cnt = tot[e];
+        const double fe = double(cnt) * inv_total;
+        const double pe = psum[it] * inv_pden;
+        a.counts[cb + e] = cnt;
+        a.offsets[long(mb) * (E + 1) + e] = lofs[e];
+        if (a.f) a.f[cb + e] = float(fe);
+        if (a.P) a.P[cb + e] = float(pe);
+        q[e] = fe * pe;
+        q[E + e] = (double(cnt) - mean) * (double(cnt) - mean);
+        q[2 * E + e] = fe > 0.0 ? -fe * log(fe) : 0.0;
+        q[3 * E + e] = double((a.capacity >= 0 && cnt > a.capacity) ? a.capacity : cnt);
+    }
+    __syncthreads();
+    constexpr int kStrides = (MOE_ROUTE_MAX_E + 63) / 64;
+    if (wave < 4) {
+        // sum of terms: f.P, squared deviations, entropy terms, kept
+        const double* v = q + wave * E;
+        double acc = 0.0;
+#pragma unroll
+        for (int i = 0; i < kStrides; ++i) {
+            const int e = lane + 64 * i;
+            acc += (e < E) ? v[e] : 0.0;
+        }
+        acc = wave_sum_f64(acc);
+        if (lane == 0) {
+            float* x = a.extra ? a.extra + long(mb) * 8 : nullptr;
+            if (wave == 0) {
+                a.aux[mb] = float(double(a.alpha) * double(E) * acc);
+                a.offsets[long(mb) * (E + 1) + E] = lofs[E];
+            } else if (wave == 1) {
+                a.cv[mb] = float(sqrt(acc / double(E)) / mean);
+            } else if (wave == 2) {
+                if (x) x[2] = float(acc);
+            } else if (x) {
+                x[3] = float(acc);
+                x[4] = float(total - acc);
+                x[5] = float(a.capacity);
+            }
+        }
+    } else if (wave < 6) {
+        // largest (wave 4) and smallest (wave 5) count
+        int m = (wave == 4) ? -1 : INT_MAX;
+#pragma unroll
+        for (int i = 0; i < kStrides; ++i) {
+            const int e = lane + 64 * i;
+            if (e < E) m = (wave == 4) ? max(m, tot[e]) : min(m, tot[e]);
+        }
+        m = (wave == 4) ? wave_max_i(m) : wave_min_i(m);
+        if (lane == 0) {
+            float* x = a.extra ? a.extra + long(mb) * 8 : nullptr;
+            if (wave == 4) {
+                a.max_over_mean[mb] = float(double(m) / mean);
+                if (x) {
+                    x[1] = float(1.0 - (double(m) - mean) / mean);
+                    x[6] = float(double(m) / total);
+                }
+            } else if (x) {
+                x[0] = float(double(m) / mean);
+                x[7] = float(double(m) / total);
+            }
+        }
+    }
+    __syncthreads();
+}
 
 // Exclusive scan of n LDS ints v[0..n) into out[0..n] (out[n] = total).
 __device__ void block_excl_scan(const int* v, int n, int* out, int* wsum) {
@@ -141,22 +243,62 @@ route_scatter_kernel(const ScatterArgs a)
         }
     };
     load_window(row_begin);
-    for (int e = tid; e < E; e += blockDim.x) {
-        // counts of the earlier splits: the first kSplitBatch loaded with the
-        // offset and the prefix, in one round
+    // per expert: the microbatch's count (the sum of its split counts) and
+    // this block's start relative to the expert's offset (the earlier splits'
+    // counts plus the prefix inside the split); the first kSplitBatch splits
+    // are loaded with the prefix, in one round, and in the first block of the
+    // microbatch with the probability sums of the statistics
+    constexpr int EPT = (MOE_ROUTE_MAX_E + NW * 64 - 1) / (NW * 64);  // experts per thread
+    const bool stats_block = bi == 0;
+    double psum[EPT];
+#pragma unroll
+    for (int it = 0; it < EPT; ++it) psum[it] = 0.0;
+    if (stats_block) {
+#pragma unroll
+        for (int it = 0; it < EPT; ++it) {
+            const int e = tid + it * NW * 64;
+            if (e >= E) break;
+            const long sb = long(mb) * a.nsplit * E + e;
+            for (int sp0 = 0; sp0 < a.nsplit; sp0 += kSplitBatch) {
+                double pv[kSplitBatch];
+#pragma unroll
+                for (int v = 0; v < kSplitBatch; ++v)
+                    pv[v] = load_or(a.split_P, sb + long(sp0 + v) * E, sp0 + v < a.nsplit, 0.0);
+#pragma unroll
+                for (int v = 0; v < kSplitBatch; ++v) psum[it] += pv[v];
+            }
+        }
+    }
+    for (int e = tid; e < E; e += NW * 64) {
         const long sb = long(mb) * a.nsplit * E + e;
-        int sv[kSplitBatch];
+        const int cp = a.colprefix[long(b) * E + e];
+        int t = 0, pre = 0;
+        for (int sp0 = 0; sp0 < a.nsplit; sp0 += kSplitBatch) {
+            int sv[kSplitBatch];
 #pragma unroll
-        for (int v = 0; v < kSplitBatch; ++v) sv[v] = load_or(a.split_tot, sb + long(v) * E, v < my_split, 0);
-        const int o = a.offsets[long(mb) * (E + 1) + e];
-        int bs = o + a.colprefix[long(b) * E + e];
+            for (int v = 0; v < kSplitBatch; ++v)
+                sv[v] = load_or(a.split_tot, sb + long(sp0 + v) * E, sp0 + v < a.nsplit, 0);
 #pragma unroll
-        for (int v = 0; v < kSplitBatch; ++v) bs += sv[v];
-        for (int sp = kSplitBatch; sp < my_split; ++sp) bs += a.split_tot[sb + long(sp) * E];
+            for (int v = 0; v < kSplitBatch; ++v) {
+                t += sv[v];
+                pre += (sp0 + v < my_split) ? sv[v] : 0;
+            }
+        }
+        tot[e] = t;
+        base[e] = pre + cp;
+    }
+    __syncthreads();
+    // offsets: exclusive prefix of the counts in expert order
+    block_excl_scan(tot, E, lofs, wsum);  // ends with a barrier
+    for (int e = tid; e < E; e += NW * 64) {
+        const int o = lofs[e];
+        base[e] += o;
         const long l = a.capacity >= 0 ? long(o) + a.capacity : long(INT32_MAX);
-        base[e] = bs;
         lim[e] = int(l < INT32_MAX ? l : INT32_MAX);
     }
+    // tot and lofs are reused by the windows only after their first
+    // barrier; the row masks' LDS is free until the first window
+    if (stats_block) microbatch_statistics<NW, EPT>(a, mb, tot, lofs, psum, reinterpret_cast<double*>(gm));
 
     uint64_t* mym = gm + wave * E;
     const int* mypre = wpre + wave * E;
@@ -246,7 +388,8 @@ size_t lds_for(int E, int NW, int rpw, int k) {
 int scatter_rows_per_wave(int E, int k) {
     const int NW = scatter_waves(E);
     int rpw = rows_cap_for_k(k);
-    while (rpw > 1 && lds_for(E, NW, rpw, k) > 160 * 1024) rpw >>= 1;
+    // (2 KB of the 160 KB left for the static LDS arrays)
+    while (rpw > 1 && lds_for(E, NW, rpw, k) > 158 * 1024) rpw >>= 1;
     return rpw;
 }
 
