@@ -246,3 +246,28 @@ def test_errors_leave_outputs_untouched():
     assert ei.value.code == lbs.MOE_ERR_WORKSPACE
     torch.cuda.synchronize()
     assert (out["topk_idx"] == -3).all()
+
+
+@pytest.mark.parametrize("T,E,k,m", [(3000, 256, 8, 1), (2000, 600, 6, 2)])
+def test_nullable_outputs(T, E, k, m):
+    """f, P, extra_stats, status, row_stats and inv_perm are nullable: with
+    them NULL the required outputs are the same bytes as with every output
+    present (E=600 takes the 8-wave scatter, two experts per thread)."""
+    print(f"case nullable T={T} E={E} k={k} m={m}", flush=True)
+    rng = np.random.default_rng(T + E)
+    L = rng.standard_normal((T, E), dtype=np.float32)
+    p_all = lbs.make_params(T, E, k, n_micro=m, capacity_factor=1.0, save_row_stats=True,
+                            inv_perm=True)
+    full = gpu_forward(p_all, {"logits": L})
+    p_min = lbs.make_params(T, E, k, n_micro=m, capacity_factor=1.0)
+    dev = torch.device("cuda:0")
+    out = lbs.alloc_outputs(p_min, device=dev)
+    for key in ("f", "P", "extra_stats", "status", "row_stats", "inv_perm"):
+        out[key] = None
+    ws = lbs.alloc_workspace(p_min, device=dev)
+    lbs.moe_route(p_min, out, ws, logits=torch.from_numpy(L).to(dev))
+    torch.cuda.synchronize()
+    for key in ("topk_idx", "topk_w", "counts", "offsets", "perm", "dropped", "aux_loss", "cv",
+                "max_over_mean"):
+        got = out[key].cpu().numpy()
+        assert np.array_equal(got.view(np.uint8), full[key].view(np.uint8)), key
