@@ -127,7 +127,23 @@ def measured_traffic(workload, kernel_prefix):
     return None
 
 
+def host_cores():
+    """Cores this process may run on, capped at the 16 a one-GPU machine shares."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def cpu_baseline(w, inp, budget_s):
+    """The serial C oracle on the host: first on one core, then on every core
+    with one contiguous token chunk per core (a thread pool over the same
+    unmodified library; ctypes releases the GIL during each call, so the
+    chunks run in parallel).  Each chunk is routed as a microbatch of its own,
+    as a data-parallel CPU router would; per-token outputs are those of the
+    whole batch."""
+    import concurrent.futures as cf
     import numpy as np
     import oracle
     L = inp["logits"] if "logits" in inp else None
@@ -137,40 +153,62 @@ def cpu_baseline(w, inp, budget_s):
     # rate on a small prefix, then a prefix sized for the budget
     n0 = min(T, max(w.n_micro, 2048 // max(1, w.n_micro) * w.n_micro))
 
-    def run(n):
-        t0 = time.perf_counter()
-        m = w.n_micro if n % w.n_micro == 0 and n == T else 1
-        if L is not None:
-            lg = L[:n]
-        else:
-            lg = oracle.gate_logits(X[:n], Wg)
+    def work(a, b, whole):
+        """Forward (+ backward, bias update) of tokens [a, b)."""
+        m = w.n_micro if whole and b - a == T else 1
+        lg = L[a:b] if L is not None else oracle.gate_logits(X[a:b], Wg)
         o = oracle.route(lg, w.k, n_micro=m, capacity_factor=w.capacity_factor, alpha=w.alpha,
                          renorm=w.renorm, select_bias=inp.get("select_bias"))
         if w.backward:
             dl = oracle.backward(lg, w.k, o["counts"], n_micro=m, alpha=w.alpha)
             if L is None:
-                oracle.gate_backward(X[:n], Wg, dl)
+                oracle.gate_backward(X[a:b], Wg, dl)
         if w.bias_gamma > 0:
-            oracle.bias_update(o["counts"], T=n, k=w.k, gamma=w.bias_gamma, bias=inp["select_bias"])
+            oracle.bias_update(o["counts"], T=b - a, k=w.k, gamma=w.bias_gamma,
+                               bias=inp["select_bias"].copy())
+
+    def run(n):
+        t0 = time.perf_counter()
+        work(0, n, True)
         return time.perf_counter() - t0
+
+    def leg(run_once, half_budget):
+        reps, elapsed = 0, 0.0
+        while elapsed < half_budget or reps == 0:
+            elapsed += run_once()
+            reps += 1
+            if reps >= 64:
+                break
+        return reps, elapsed
 
     t_small = run(n0)
     n = int(min(T, max(n0, n0 * budget_s / max(t_small, 1e-6))))
-    reps, tokens, elapsed = 0, 0, 0.0
-    while elapsed < budget_s * 0.5 or reps == 0:
-        elapsed += run(n)
-        tokens += n
-        reps += 1
-        if reps >= 64:
-            break
-    sample = (f"oracle (serial C, fp64) on the first {n} tokens of the seed-0 {w.name} inputs"
-              f" x{reps} pass(es): forward" + (" + backward" if w.backward else "")
-              + (" incl. gate GEMM" if w.d > 0 else "")
-              + (" and its backward" if w.d > 0 and w.backward else "")
-              + (" with selection bias" if w.select_bias_scale > 0 else "")
-              + (" + bias update" if w.bias_gamma > 0 else ""))
-    return {"value": tokens / elapsed, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": sample, "seconds": round(elapsed, 2)}
+    reps, elapsed = leg(lambda: run(n), budget_s * 0.5)
+    serial = n * reps / elapsed
+
+    cores = host_cores()
+    chunk = max(1, n // cores)
+    bounds = [(i * chunk, (i + 1) * chunk if i < cores - 1 else n) for i in range(cores)]
+    bounds = [(a, b) for a, b in bounds if b > a]
+    with cf.ThreadPoolExecutor(len(bounds)) as ex:
+        def run_all():
+            t0 = time.perf_counter()
+            list(ex.map(lambda ab: work(ab[0], ab[1], False), bounds))
+            return time.perf_counter() - t0
+        reps_p, elapsed_p = leg(run_all, budget_s * 0.5)
+    parallel = n * reps_p / elapsed_p
+
+    what = (f"the first {n} tokens of the seed-0 {w.name} inputs: forward"
+            + (" + backward" if w.backward else "")
+            + (" incl. gate GEMM" if w.d > 0 else "")
+            + (" and its backward" if w.d > 0 and w.backward else "")
+            + (" with selection bias" if w.select_bias_scale > 0 else "")
+            + (" + bias update" if w.bias_gamma > 0 else ""))
+    sample = (f"oracle (serial C, fp64) on {what}; {len(bounds)} threads each routing one "
+              f"contiguous chunk of ~{chunk} tokens as its own microbatch, x{reps_p} pass(es)")
+    return {"value": parallel, "unit": "tokens/s", "cores": len(bounds), "kind": "oracle",
+            "sample": sample, "seconds": round(elapsed_p, 2),
+            "serial": {"value": serial, "cores": 1, "passes": reps, "seconds": round(elapsed, 2)}}
 
 
 PLANNERS = ("eplb_v4", "sinkhorn_r64")
