@@ -445,6 +445,10 @@ def main():
                    "backward_ms": None if bwd_ms is None else round(bwd_ms, 5),
                    "gate_backward_ms": None if gb_ms is None else round(gb_ms, 5),
                    "copy_ceiling_GBps": round(copy_gbps, 1),
+                   # the dominant kernel against the copy ceiling measured here
+                   "frac_of_copy_ceiling": round(achieved / copy_gbps, 4),
+                   # the step without the backward kernels' event spans
+                   "forward_ms": round(ms_step - (bwd_ms or 0.0) - (gb_ms or 0.0), 5),
                    "assignments_per_s": w.T * w.k / (ms_step * 1e-3),
                    "input_copies": ncopy, "host_enqueue_s": round(host_s, 4),
                    "status": status},
