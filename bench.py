@@ -409,7 +409,11 @@ def main():
         dom_name, dom_bytes, dom_ms = "route_backward_kernel", ab["route_backward"], bwd_ms
     else:
         dom_name, dom_bytes, dom_ms = "route_rows_kernel", ab["rows"], rows_ms
-    traffic = measured_traffic(w.name, dom_name) if w.d == 0 else None
+    if gate_bwd:  # the kernel the gate backward launches for this E (its reduce step aside)
+        traffic = measured_traffic(w.name, "moe::gate_backward_mfma_kernel" if w.E <= 16
+                                   else "moe::gate_backward_kernel<")
+    else:
+        traffic = measured_traffic(w.name, dom_name) if w.d == 0 else None
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     step_bytes = ab["forward"] + ab["backward"]
 
