@@ -123,6 +123,26 @@ def test_gate_small():
     inp, p, g, r = _gate_case(w, 0)
 
 
+@pytest.mark.parametrize("T,d,E", [(1003, 520, 8), (77, 4096, 16), (130, 264, 12), (1000, 512, 40),
+                                   (1, 8, 1)])
+def test_gate_logits_shapes(T, d, E):
+    """Gate GEMM alone over ragged shapes: T not a multiple of the 64-token
+    block, d not a multiple of 32, E = 16 (full tile), E = 40 (three expert
+    tiles, the wide kernel), a single token and a single 8-wide k step."""
+    print(f"case gate_logits T={T} d={d} E={E}", flush=True)
+    rng = np.random.default_rng(T + d + E)
+    f32 = rng.standard_normal((T, d)).astype(np.float32)
+    w32 = (0.05 * rng.standard_normal((d, E))).astype(np.float32)
+    bf = lambda a: ((a.view(np.uint32) + 0x7FFF + ((a.view(np.uint32) >> 16) & 1)) >> 16).astype(np.uint16)
+    X, Wg = bf(f32), bf(w32)
+    k = min(2, E)
+    p = lbs.make_params(T, E, k, d=d, capacity_factor=1.25)
+    g = gpu_forward(p, {"X": X, "Wg": Wg})
+    ref = oracle.gate_logits(X, Wg)
+    err = np.abs(g["logits"].astype(np.float64) - ref)
+    assert err.max() <= 1e-4, f"gate logits max error {err.max()}"
+
+
 def test_gate_full():
     w = WORKLOADS["gate_top2"]
     print("case gate_full", flush=True)
