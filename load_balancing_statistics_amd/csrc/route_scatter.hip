@@ -19,15 +19,14 @@
 // run being bit r of a 64-bit mask per (wave, expert).  The lanes of a row
 // hold contiguous chunks of its k slots, read as 16-byte vectors when the
 // chunks are whole vectors (every load instruction then covers contiguous
-// bytes).  Every slot (r, j)
-// ORs its bit into the mask of its expert; a slot's rank among the wave's
-// assignments to that expert is then the popcount of the mask below its bit,
-// and the wave's count is the whole popcount.  An exclusive scan over the
-// waves and one over the experts place every slot in an LDS copy of the
-// window sorted by expert, which is written to the permutation in that order:
-// the block's assignments to one expert land in consecutive words, so the
-// stores coalesce.  dropped and inv_perm are indexed by the assignment and
-// are stored from the ranking pass.
+// bytes).  Every slot (r, j) ORs its bit into the mask of its expert; a
+// slot's rank among the wave's assignments to that expert is then the
+// popcount of the mask below its bit, and the wave's count is the whole
+// popcount.  An exclusive scan over the waves and one over the experts place
+// every slot in an LDS copy of the window sorted by expert, which is written
+// to the permutation in that order: the block's assignments to one expert
+// land in consecutive words, so the stores coalesce.  dropped and inv_perm
+// are indexed by the assignment and are stored from the ranking pass.
 #include <climits>
 
 #include "route_common.hpp"
