@@ -155,6 +155,7 @@ int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
     ra.qcap = moe::rows_queue_cap(c);
     ra.topk_idx = out->topk_idx; ra.topk_w = out->topk_w; ra.row_stats = out->row_stats;
     ra.cnt_part = ws.cnt_part; ra.P_part = ws.P_part; ra.flag_part = ws.flag_part;
+    ra.status = out->status;
     const bool timed = out->row_pass_events[0] && out->row_pass_events[1];
     if (timed && hipEventRecord(static_cast<hipEvent_t>(out->row_pass_events[0]), st) != hipSuccess)
         return MOE_ERR_HIP;
@@ -168,11 +169,15 @@ int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
     sa.nsplit = c.nsplit;
     sa.colprefix = ws.colprefix; sa.split_tot = ws.split_tot; sa.split_P = ws.split_P;
     sa.status = out->status;
-    if (moe::launch_route_scan(c, sa, st) != hipSuccess) return MOE_ERR_HIP;
+    // few row blocks per microbatch: the scatter sums their partials itself
+    const int fold_q = moe::scatter_fold_groups(p->E, p->k, c.bpm);
+    if (fold_q == 0 && moe::launch_route_scan(c, sa, st) != hipSuccess) return MOE_ERR_HIP;
 
     moe::ScatterArgs ca{};
     ca.topk_idx = out->topk_idx; ca.colprefix = ws.colprefix; ca.split_tot = ws.split_tot;
     ca.split_P = ws.split_P;
+    ca.cnt_part = ws.cnt_part; ca.P_part = ws.P_part; ca.flag_part = ws.flag_part;
+    ca.fold_q = fold_q; ca.B = c.B;
     ca.alpha = p->alpha;
     ca.p_masked = (p->flags & MOE_P_MASKED) ? 1 : 0;
     ca.counts = out->counts; ca.offsets = out->offsets; ca.f = out->f; ca.P = out->P;

@@ -188,6 +188,7 @@ struct RowsArgs {
     int32_t* cnt_part;
     float* P_part;
     int32_t* flag_part;
+    int32_t* status;  // nullable; zeroed by block 0 (the later kernels OR bits in)
 };
 
 struct ScanArgs {
@@ -203,9 +204,14 @@ struct ScanArgs {
 
 struct ScatterArgs {
     const int32_t* topk_idx;
-    const int32_t* colprefix;
+    const int32_t* colprefix;   // from the block combine (fold_q == 0)
     const int32_t* split_tot;
     const double* split_P;
+    const int32_t* cnt_part;    // the row pass's partials (fold_q > 0)
+    const float* P_part;
+    const int32_t* flag_part;
+    int fold_q;  // > 0: sum the row pass's partials here, in fold_q groups of row blocks
+    int B;       // row blocks in total
     int T, E, k, Tm, bpm, nsplit;
     int rows_per_wave;  // rows a wave ranks per window (<= 64, one mask bit each)
     int capacity;  // < 0: unlimited
@@ -310,6 +316,7 @@ hipError_t launch_route_scan(const RowCfg& c, const ScanArgs& a, hipStream_t st)
 hipError_t launch_route_scatter(const RowCfg& c, const ScatterArgs& a, hipStream_t st);
 int scatter_rows_per_wave(int E, int k);
 size_t scatter_lds_bytes(int E, int k);
+int scatter_fold_groups(int E, int k, int bpm);
 hipError_t launch_route_backward(const RowCfg& c, const BackArgs& a, hipStream_t st);
 hipError_t launch_bias_update(const BiasArgs& a, hipStream_t st);
 hipError_t launch_gate_backward(const GateBackArgs& a, hipStream_t st);

@@ -437,6 +437,7 @@ route_rows_kernel(const RowsArgs a)
     block_rows(blockIdx.x, a.bpm, a.Tm, row_begin, row_end);
 
     for (int e = tid; e < E; e += NW * 64) hist[e] = 0;
+    if (a.status && blockIdx.x == 0 && tid == 0) a.status[0] = 0;
     if constexpr (BIAS)
         for (int e = tid; e < E; e += NW * 64) blds[e] = a.bias[e];
     if (a.p_masked)

@@ -38,6 +38,8 @@ using namespace dev;
 
 constexpr int kScatMaxWaves = 16;
 constexpr int kSplitBatch = 8;
+constexpr int kFoldLoads = 16;  // row blocks a thread sums when the scatter folds the combine in
+constexpr int kFoldGroups = 2;  // at most this many row-block groups per expert
 
 // Counts, offsets and balance statistics of microbatch mb, by one block of
 // NW waves, from the counts tot[0..E) and their exclusive prefix lofs[0..E]
@@ -252,6 +254,68 @@ route_scatter_kernel(const ScatterArgs a)
     double psum[EPT];
 #pragma unroll
     for (int it = 0; it < EPT; ++it) psum[it] = 0.0;
+    if (a.fold_q > 0) {
+        // Few row blocks per microbatch: every block sums the row pass's
+        // partials itself and no combine kernel runs.  Thread t < Q*E takes
+        // expert t % E over the row blocks [q*bpm/Q, (q+1)*bpm/Q), q = t / E
+        // (at most kFoldLoads of them, loaded in one round); the Q groups meet
+        // in LDS -- the row masks' area, free until the first window -- and
+        // are added in group order.
+        const int Q = a.fold_q;
+        int* fpre = reinterpret_cast<int*>(gm);
+        int* ftot = fpre + Q * E;
+        double* fps = reinterpret_cast<double*>(ftot + Q * E);
+        const long pb = long(mb) * a.bpm;  // the microbatch's first row block
+        for (int t = tid; t < Q * E; t += NW * 64) {
+            const int e = t % E, q = t / E;
+            const int b0 = (q * a.bpm) / Q, b1 = ((q + 1) * a.bpm) / Q;
+            int cv[kFoldLoads];
+            float pv[kFoldLoads];
+#pragma unroll
+            for (int v = 0; v < kFoldLoads; ++v) {
+                const long o = (pb + ((b0 + v < b1) ? b0 + v : b0)) * E + e;
+                cv[v] = a.cnt_part[o];
+                pv[v] = a.P_part[o];
+            }
+            int pre = 0, tt = 0;
+            double ps = 0.0;
+#pragma unroll
+            for (int v = 0; v < kFoldLoads; ++v) {
+                if (b0 + v < b1) {
+                    tt += cv[v];
+                    pre += (b0 + v < bi) ? cv[v] : 0;
+                    ps += double(pv[v]);
+                }
+            }
+            fpre[t] = pre;
+            ftot[t] = tt;
+            fps[t] = ps;
+        }
+        // status: the flags of every row block, by logical block 0 (the row
+        // pass zeroed the word; the scatter only ORs bits into it)
+        if (a.status && b == 0) {
+            int fl = 0;
+            for (int j = tid; j < a.B; j += NW * 64) fl |= a.flag_part[j];
+            if (__syncthreads_or(fl & MOE_STATUS_NONFINITE) && tid == 0)
+                atomicOr(a.status, MOE_STATUS_NONFINITE);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int it = 0; it < EPT; ++it) {
+            const int e = tid + it * NW * 64;
+            if (e >= E) break;
+            int pre = 0, tt = 0;
+            double ps = 0.0;
+            for (int q = 0; q < Q; ++q) {
+                pre += fpre[q * E + e];
+                tt += ftot[q * E + e];
+                ps += fps[q * E + e];
+            }
+            tot[e] = tt;
+            base[e] = pre;
+            psum[it] = ps;
+        }
+    } else {
     if (stats_block) {
 #pragma unroll
         for (int it = 0; it < EPT; ++it) {
@@ -285,6 +349,7 @@ route_scatter_kernel(const ScatterArgs a)
         }
         tot[e] = t;
         base[e] = pre + cp;
+    }
     }
     __syncthreads();
     // offsets: exclusive prefix of the counts in expert order
@@ -381,6 +446,21 @@ size_t lds_for(int E, int NW, int rpw, int k) {
 }
 
 }  // namespace
+
+// Row-block groups for folding the block combine into the scatter: enough
+// groups that a thread sums at most kFoldLoads row blocks, when that takes at
+// most kFoldGroups groups, the groups of every expert fit the block's
+// threads and their sums (16 bytes each) the LDS free before the first
+// window; 0 otherwise (the combine kernel runs).  Measured: folding saves
+// 2-3 us a call with one or two groups; with 16 (65536 tokens over 256 row
+// blocks, E=64) the combine in LDS cost what the kernel launch saved.
+int scatter_fold_groups(int E, int k, int bpm) {
+    const int NW = scatter_waves(E);
+    const long Q = (bpm + kFoldLoads - 1) / kFoldLoads;
+    const size_t room = size_t(NW) * E * 12 + size_t(NW) * scatter_rows_per_wave(E, k) * k * 8;
+    if (Q < 1 || Q > kFoldGroups || Q * E > long(NW) * 64 || size_t(16) * Q * E > room) return 0;
+    return int(Q);
+}
 
 // Rows per wave and window: 64 (one mask bit per row), halved until the
 // block's LDS fits.
