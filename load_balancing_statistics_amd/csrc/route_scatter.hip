@@ -244,11 +244,9 @@ route_scatter_kernel(const ScatterArgs a)
         }
     };
     load_window(row_begin);
-    // per expert: the microbatch's count (the sum of its split counts) and
-    // this block's start relative to the expert's offset (the earlier splits'
-    // counts plus the prefix inside the split); the first kSplitBatch splits
-    // are loaded with the prefix, in one round, and in the first block of the
-    // microbatch with the probability sums of the statistics
+    // per expert: the microbatch's count tot[e], this block's start relative
+    // to the expert's offset base[e] (the count in the microbatch's earlier
+    // row blocks) and, for the statistics, the probability sum psum
     constexpr int EPT = (MOE_ROUTE_MAX_E + NW * 64 - 1) / (NW * 64);  // experts per thread
     const bool stats_block = bi == 0;
     double psum[EPT];
@@ -316,40 +314,44 @@ route_scatter_kernel(const ScatterArgs a)
             psum[it] = ps;
         }
     } else {
-    if (stats_block) {
+        // From the combine kernel: the split sums and this block's prefix
+        // inside its split; the first kSplitBatch splits are loaded with the
+        // prefix, in one round, and in the first block of the microbatch
+        // with the probability sums.
+        if (stats_block) {
 #pragma unroll
-        for (int it = 0; it < EPT; ++it) {
-            const int e = tid + it * NW * 64;
-            if (e >= E) break;
+            for (int it = 0; it < EPT; ++it) {
+                const int e = tid + it * NW * 64;
+                if (e >= E) break;
+                const long sb = long(mb) * a.nsplit * E + e;
+                for (int sp0 = 0; sp0 < a.nsplit; sp0 += kSplitBatch) {
+                    double pv[kSplitBatch];
+#pragma unroll
+                    for (int v = 0; v < kSplitBatch; ++v)
+                        pv[v] = load_or(a.split_P, sb + long(sp0 + v) * E, sp0 + v < a.nsplit, 0.0);
+#pragma unroll
+                    for (int v = 0; v < kSplitBatch; ++v) psum[it] += pv[v];
+                }
+            }
+        }
+        for (int e = tid; e < E; e += NW * 64) {
             const long sb = long(mb) * a.nsplit * E + e;
+            const int cp = a.colprefix[long(b) * E + e];
+            int t = 0, pre = 0;
             for (int sp0 = 0; sp0 < a.nsplit; sp0 += kSplitBatch) {
-                double pv[kSplitBatch];
+                int sv[kSplitBatch];
 #pragma unroll
                 for (int v = 0; v < kSplitBatch; ++v)
-                    pv[v] = load_or(a.split_P, sb + long(sp0 + v) * E, sp0 + v < a.nsplit, 0.0);
+                    sv[v] = load_or(a.split_tot, sb + long(sp0 + v) * E, sp0 + v < a.nsplit, 0);
 #pragma unroll
-                for (int v = 0; v < kSplitBatch; ++v) psum[it] += pv[v];
+                for (int v = 0; v < kSplitBatch; ++v) {
+                    t += sv[v];
+                    pre += (sp0 + v < my_split) ? sv[v] : 0;
+                }
             }
+            tot[e] = t;
+            base[e] = pre + cp;
         }
-    }
-    for (int e = tid; e < E; e += NW * 64) {
-        const long sb = long(mb) * a.nsplit * E + e;
-        const int cp = a.colprefix[long(b) * E + e];
-        int t = 0, pre = 0;
-        for (int sp0 = 0; sp0 < a.nsplit; sp0 += kSplitBatch) {
-            int sv[kSplitBatch];
-#pragma unroll
-            for (int v = 0; v < kSplitBatch; ++v)
-                sv[v] = load_or(a.split_tot, sb + long(sp0 + v) * E, sp0 + v < a.nsplit, 0);
-#pragma unroll
-            for (int v = 0; v < kSplitBatch; ++v) {
-                t += sv[v];
-                pre += (sp0 + v < my_split) ? sv[v] : 0;
-            }
-        }
-        tot[e] = t;
-        base[e] = pre + cp;
-    }
     }
     __syncthreads();
     // offsets: exclusive prefix of the counts in expert order
