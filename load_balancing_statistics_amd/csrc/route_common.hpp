@@ -60,18 +60,21 @@ inline RowCfg choose_rows(int T, int E, int k, int n_micro, bool bias = false) {
     }
     // unaligned rows take the generic (bounds-checked) column path
     c.PAD = (S * c.G != E || c.VEC == 1) ? 1 : 0;
-    // One block per compute unit holding as many waves as the row pass's
-    // registers allow: 16 (4 per SIMD) when a lane owns up to 16 columns,
-    // 12 when it owns 24.
+    // As many waves per compute unit as the row pass's registers allow: 16
+    // (4 per SIMD) when a lane owns up to 16 columns, as two blocks of 8
+    // (blocks of half the rows: the combine and the scatter that follow
+    // work per row block, and the scatter's smaller blocks overlap two per
+    // compute unit; measured 1.5 us less a step at E=256 top-8 than one
+    // block of 16), 12 in one block when a lane owns 24.
     // The selection-bias variant keeps G more registers per lane: 12 waves
     // when a lane owns up to 16 columns, 8 when it owns 24.
     // One or two lanes per row with 16 columns hold more per-row state per
     // lane (ranking passes): 12 waves there too, so nothing spills.
-    c.NW = bias ? ((c.G > 16) ? 8 : 12) : ((c.G > 16 || (S <= 2 && c.G >= 16)) ? 12 : 16);
+    c.NW = bias ? ((c.G > 16) ? 8 : 12) : ((c.G > 16 || (S <= 2 && c.G >= 16)) ? 12 : 8);
     const int W = 64 / S;
     const long per_iter = long(c.NW) * W;
     const long Tm = T / n_micro;
-    const long blocks_per_cu = 1;
+    const long blocks_per_cu = (!bias && c.NW == 8) ? 2 : 1;
     const long target = kAssumedCUs * blocks_per_cu;
     // balanced split: every block of a microbatch gets floor or ceil of
     // Tm / bpm rows, at least one row group per wave iteration

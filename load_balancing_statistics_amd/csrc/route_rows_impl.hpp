@@ -410,8 +410,14 @@ struct RowPass {
     }
 };
 
+// Waves per SIMD the row pass must fit: 4 for the eight-wave blocks that run
+// two per compute unit (128 registers, as one block of 16 had), else 1.
+template <int NW, bool BIAS>
+constexpr int rows_min_waves_per_simd() { return (NW == 8 && !BIAS) ? 4 : 1; }
+
 template <int S, int G, int VEC, bool PAD, int NW, bool BIAS>
 __global__ void __launch_bounds__(NW * 64)
+__attribute__((amdgpu_waves_per_eu(rows_min_waves_per_simd<NW, BIAS>())))
 route_rows_kernel(const RowsArgs a)
 {
     using RP = RowPass<S, G, VEC, PAD, NW, BIAS>;
@@ -726,7 +732,7 @@ hipError_t launch_rows(const RowCfg& c, const RowsArgs& a, hipStream_t st) {
         if (c.NW == 8) return launch_rows_nw<S, G, VEC, PAD, 8, true>(c, a, st);
         return hipErrorInvalidValue;
     }
-    if (c.NW == 16) return launch_rows_nw<S, G, VEC, PAD, 16, false>(c, a, st);
+    if (c.NW == 8) return launch_rows_nw<S, G, VEC, PAD, 8, false>(c, a, st);
     if (c.NW == 12) return launch_rows_nw<S, G, VEC, PAD, 12, false>(c, a, st);
     return hipErrorInvalidValue;
 }
@@ -747,9 +753,9 @@ hipError_t launch_backward_nw(const RowCfg& c, const BackArgs& a, hipStream_t st
 template <int S, int G, int VEC, bool PAD>
 hipError_t launch_backward(const RowCfg& c, const BackArgs& a, hipStream_t st) {
     const bool sp = a.p_masked || a.d_topk_w;
-    if (c.NW == 16)
-        return sp ? launch_backward_nw<S, G, VEC, PAD, 16, true>(c, a, st)
-                  : launch_backward_nw<S, G, VEC, PAD, 16, false>(c, a, st);
+    if (c.NW == 8)
+        return sp ? launch_backward_nw<S, G, VEC, PAD, 8, true>(c, a, st)
+                  : launch_backward_nw<S, G, VEC, PAD, 8, false>(c, a, st);
     return sp ? launch_backward_nw<S, G, VEC, PAD, 12, true>(c, a, st)
               : launch_backward_nw<S, G, VEC, PAD, 12, false>(c, a, st);
 }

@@ -36,7 +36,7 @@ namespace {
 
 using namespace dev;
 
-constexpr int kScatMaxWaves = 16;
+constexpr int kScatMaxWaves = 8;
 constexpr int kSplitBatch = 8;
 constexpr int kFoldLoads = 16;  // row blocks a thread sums when the scatter folds the combine in
 constexpr int kFoldGroups = 2;  // at most this many row-block groups per expert
@@ -433,7 +433,9 @@ route_scatter_kernel(const ScatterArgs a)
     if (internal && a.status) atomicOr(a.status, MOE_STATUS_INTERNAL);
 }
 
-int scatter_waves(int E) { return E <= 512 ? 16 : 8; }
+// Eight waves: the blocks' LDS-bound phases and barriers overlap two blocks
+// per compute unit wherever their LDS fits (E=256 top-8: 61.5 KB a block).
+int scatter_waves(int E) { (void)E; return 8; }
 
 int rows_cap_for_k(int k) {
     int lanes = 1;
@@ -495,7 +497,8 @@ hipError_t launch_route_scatter(const RowCfg& c, const ScatterArgs& a, hipStream
     if (a.k > MOE_ROUTE_MAX_K || a.E > MOE_ROUTE_MAX_E || a.rows_per_wave < 1 ||
         a.rows_per_wave > rows_cap_for_k(a.k))
         return hipErrorInvalidValue;
-    return NW == 16 ? launch_scatter_nw<16>(c, a, lds, st) : launch_scatter_nw<8>(c, a, lds, st);
+    if (NW != 8) return hipErrorInvalidValue;
+    return launch_scatter_nw<8>(c, a, lds, st);
 }
 
 }  // namespace moe
