@@ -32,7 +32,7 @@ int check_shape(const moe_route_params* p) {
     const RowCfg c = moe::choose_rows(p->T, p->E, p->k, p->n_micro, bias);
     const bool masked = (p->flags & MOE_P_MASKED) != 0;
     if (c.G < 0 || moe::rows_lds_bytes(c, p->E, p->k, bias, masked) > kMaxLds) return MOE_ERR_UNSUPPORTED;
-    if (moe::scatter_lds_bytes(p->E, p->k) > kMaxLds) return MOE_ERR_UNSUPPORTED;
+    if (moe::scatter_lds_bytes(p->E, p->k, moe::scatter_waves(p->E, c.NW)) > kMaxLds) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -170,21 +170,22 @@ int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
     sa.colprefix = ws.colprefix; sa.split_tot = ws.split_tot; sa.split_P = ws.split_P;
     sa.status = out->status;
     // few row blocks per microbatch: the scatter sums their partials itself
-    const int fold_q = moe::scatter_fold_groups(p->E, p->k, c.bpm);
+    const int scat_nw = moe::scatter_waves(p->E, c.NW);
+    const int fold_q = moe::scatter_fold_groups(p->E, p->k, c.bpm, scat_nw);
     if (fold_q == 0 && moe::launch_route_scan(c, sa, st) != hipSuccess) return MOE_ERR_HIP;
 
     moe::ScatterArgs ca{};
     ca.topk_idx = out->topk_idx; ca.colprefix = ws.colprefix; ca.split_tot = ws.split_tot;
     ca.split_P = ws.split_P;
     ca.cnt_part = ws.cnt_part; ca.P_part = ws.P_part; ca.flag_part = ws.flag_part;
-    ca.fold_q = fold_q; ca.B = c.B;
+    ca.fold_q = fold_q; ca.B = c.B; ca.nw = scat_nw;
     ca.alpha = p->alpha;
     ca.p_masked = (p->flags & MOE_P_MASKED) ? 1 : 0;
     ca.counts = out->counts; ca.offsets = out->offsets; ca.f = out->f; ca.P = out->P;
     ca.aux = out->aux_loss; ca.cv = out->cv; ca.max_over_mean = out->max_over_mean;
     ca.extra = out->extra_stats;
     ca.T = p->T; ca.E = p->E; ca.k = p->k; ca.Tm = Tm; ca.bpm = c.bpm; ca.nsplit = c.nsplit;
-    ca.rows_per_wave = moe::scatter_rows_per_wave(p->E, p->k);
+    ca.rows_per_wave = moe::scatter_rows_per_wave(p->E, p->k, scat_nw);
     ca.capacity = int(capacity_of(p));
     ca.vec_idx = (p->k % 4 == 0 && aligned(out->topk_idx, 16)) ? 1 : 0;
     ca.perm = out->perm;

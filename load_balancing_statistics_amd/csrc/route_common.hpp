@@ -214,6 +214,7 @@ struct ScatterArgs {
     const float* P_part;
     const int32_t* flag_part;
     int fold_q;  // > 0: sum the row pass's partials here, in fold_q groups of row blocks
+    int nw;      // waves per block (scatter_waves)
     int B;       // row blocks in total
     int T, E, k, Tm, bpm, nsplit;
     int rows_per_wave;  // rows a wave ranks per window (<= 64, one mask bit each)
@@ -317,9 +318,10 @@ MOE_DECLARE_SEGMENT(16) MOE_DECLARE_SEGMENT(32) MOE_DECLARE_SEGMENT(64)
 #undef MOE_DECLARE_SEGMENT
 hipError_t launch_route_scan(const RowCfg& c, const ScanArgs& a, hipStream_t st);
 hipError_t launch_route_scatter(const RowCfg& c, const ScatterArgs& a, hipStream_t st);
-int scatter_rows_per_wave(int E, int k);
-size_t scatter_lds_bytes(int E, int k);
-int scatter_fold_groups(int E, int k, int bpm);
+int scatter_waves(int E, int row_nw);
+int scatter_rows_per_wave(int E, int k, int NW);
+size_t scatter_lds_bytes(int E, int k, int NW);
+int scatter_fold_groups(int E, int k, int bpm, int NW);
 hipError_t launch_route_backward(const RowCfg& c, const BackArgs& a, hipStream_t st);
 hipError_t launch_bias_update(const BiasArgs& a, hipStream_t st);
 hipError_t launch_gate_backward(const GateBackArgs& a, hipStream_t st);

@@ -36,7 +36,7 @@ namespace {
 
 using namespace dev;
 
-constexpr int kScatMaxWaves = 8;
+constexpr int kScatMaxWaves = 16;
 constexpr int kSplitBatch = 8;
 constexpr int kFoldLoads = 16;  // row blocks a thread sums when the scatter folds the combine in
 constexpr int kFoldGroups = 2;  // at most this many row-block groups per expert
@@ -433,9 +433,6 @@ route_scatter_kernel(const ScatterArgs a)
     if (internal && a.status) atomicOr(a.status, MOE_STATUS_INTERNAL);
 }
 
-// Eight waves: the blocks' LDS-bound phases and barriers overlap two blocks
-// per compute unit wherever their LDS fits (E=256 top-8: 61.5 KB a block).
-int scatter_waves(int E) { (void)E; return 8; }
 
 int rows_cap_for_k(int k) {
     int lanes = 1;
@@ -458,27 +455,33 @@ size_t lds_for(int E, int NW, int rpw, int k) {
 // window; 0 otherwise (the combine kernel runs).  Measured: folding saves
 // 2-3 us a call with one or two groups; with 16 (65536 tokens over 256 row
 // blocks, E=64) the combine in LDS cost what the kernel launch saved.
-int scatter_fold_groups(int E, int k, int bpm) {
-    const int NW = scatter_waves(E);
+int scatter_fold_groups(int E, int k, int bpm, int NW) {
     const long Q = (bpm + kFoldLoads - 1) / kFoldLoads;
-    const size_t room = size_t(NW) * E * 12 + size_t(NW) * scatter_rows_per_wave(E, k) * k * 8;
+    const size_t room = size_t(NW) * E * 12 + size_t(NW) * scatter_rows_per_wave(E, k, NW) * k * 8;
     if (Q < 1 || Q > kFoldGroups || Q * E > long(NW) * 64 || size_t(16) * Q * E > room) return 0;
     return int(Q);
 }
 
 // Rows per wave and window: 64 (one mask bit per row), halved until the
 // block's LDS fits.
-int scatter_rows_per_wave(int E, int k) {
-    const int NW = scatter_waves(E);
+int scatter_rows_per_wave(int E, int k, int NW) {
     int rpw = rows_cap_for_k(k);
     // (2 KB of the 160 KB left for the static LDS arrays)
     while (rpw > 1 && lds_for(E, NW, rpw, k) > 158 * 1024) rpw >>= 1;
     return rpw;
 }
 
-size_t scatter_lds_bytes(int E, int k) {
-    return lds_for(E, scatter_waves(E), scatter_rows_per_wave(E, k), k);
+size_t scatter_lds_bytes(int E, int k, int NW) {
+    return lds_for(E, NW, scatter_rows_per_wave(E, k, NW), k);
 }
+
+// Waves per scatter block, following the row pass's blocks (the scatter's
+// block b takes row block b's rows): eight when the row pass runs two blocks
+// of eight per compute unit -- half the rows a block, and two scatter blocks
+// share a compute unit and overlap their LDS-bound phases and barriers --,
+// sixteen when it runs one block, so that one window covers a row block;
+// eight above E = 512, where sixteen waves' row masks do not fit the LDS.
+int scatter_waves(int E, int row_nw) { return (row_nw == 8 || E > 512) ? 8 : 16; }
 
 template <int NW>
 hipError_t launch_scatter_nw(const RowCfg& c, const ScatterArgs& a, size_t lds, hipStream_t st) {
@@ -492,13 +495,14 @@ hipError_t launch_scatter_nw(const RowCfg& c, const ScatterArgs& a, size_t lds, 
 }
 
 hipError_t launch_route_scatter(const RowCfg& c, const ScatterArgs& a, hipStream_t st) {
-    const int NW = scatter_waves(a.E);
+    const int NW = a.nw;
     const size_t lds = lds_for(a.E, NW, a.rows_per_wave, a.k);
     if (a.k > MOE_ROUTE_MAX_K || a.E > MOE_ROUTE_MAX_E || a.rows_per_wave < 1 ||
         a.rows_per_wave > rows_cap_for_k(a.k))
         return hipErrorInvalidValue;
-    if (NW != 8) return hipErrorInvalidValue;
-    return launch_scatter_nw<8>(c, a, lds, st);
+    if (NW == 16) return launch_scatter_nw<16>(c, a, lds, st);
+    if (NW == 8) return launch_scatter_nw<8>(c, a, lds, st);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace moe
