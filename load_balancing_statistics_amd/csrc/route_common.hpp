@@ -42,9 +42,10 @@ inline int next_pow2(int v) {
 }
 
 // Pick the lane mapping: the narrowest segment (S >= k, power of two) whose
-// per-lane column count fits the table.  Then the rows per block: about two
-// or three resident blocks per compute unit over the whole batch, so the
-// grid is one wave of blocks and the per-block partials stay few.
+// per-lane column count fits the table.  Then the waves per block and the
+// rows per block: one or two resident blocks per compute unit over the whole
+// batch, so the grid is one wave of blocks and the per-block partials stay
+// few.
 inline RowCfg choose_rows(int T, int E, int k, int n_micro, bool bias = false) {
     RowCfg c{};
     c.VEC = (E % 4 == 0) ? 4 : 1;
