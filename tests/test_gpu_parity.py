@@ -177,6 +177,8 @@ EDGE = [
     (1024, 64, 2, 1, 1.0, -1, True, "signed_zero"),  # -0.0 / +0.0 ties
     (1024, 8, 1, 1, 1.25, -1, False, "quantized"),
     (700, 12, 5, 1, 1.0, -1, True, "quantized"),
+    (2000, 250, 8, 1, 1.25, -1, True, "normal"),     # 16 lanes x 16 columns, scalar loads
+    (3000, 130, 6, 2, 1.0, -1, False, "normal"),     # padded columns, two microbatches
 ]
 
 
