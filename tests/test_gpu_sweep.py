@@ -9,7 +9,9 @@ import numpy as np
 import pytest
 
 import load_balancing_statistics_amd as lbs
-from gpu_helpers import compare_forward, gpu_forward, oracle_forward
+import oracle
+from gpu_helpers import (backward_tolerance, compare_forward, gpu_backward, gpu_forward,
+                         oracle_forward)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,3 +41,25 @@ def test_forward_sweep(T, E, k, m, cf, renorm):
     g = gpu_forward(p, {"logits": L})
     r = oracle_forward(p, L)
     compare_forward(g, r, p)
+
+
+@pytest.mark.parametrize("T,E,k,m,cf,renorm", _cases(12, seed=77),
+                         ids=[f"T{c[0]}_E{c[1]}_k{c[2]}_m{c[3]}" for c in _cases(12, seed=77)])
+def test_backward_sweep(T, E, k, m, cf, renorm):
+    """The aux-loss gradient over the same kind of shapes, with and without
+    the saved row statistics, per-microbatch upstream gradients."""
+    print(f"case backward sweep T={T} E={E} k={k} m={m}", flush=True)
+    rng = np.random.default_rng(T * 3 + E)
+    L = (rng.standard_normal((T, E)) + rng.normal(0.0, 0.7, E)).astype(np.float32)
+    p = lbs.make_params(T, E, k, n_micro=m, capacity_factor=cf, renorm=renorm,
+                        save_row_stats=True, inv_perm=True)
+    g = gpu_forward(p, {"logits": L})
+    r = oracle_forward(p, L)
+    d_aux = np.linspace(0.5, 2.0, m)
+    ref = oracle.backward(L, k, r["counts"], n_micro=m, alpha=p.alpha, d_aux=d_aux)
+    scale = backward_tolerance(L, r, r["counts"], p, d_aux)
+    for stats in (g["row_stats"], None):
+        dl = gpu_backward(p, L, g["counts"], row_stats=stats, d_aux=d_aux)
+        err = np.abs(dl.astype(np.float64) - ref)
+        bound = 1e-5 * np.maximum(np.abs(ref), scale) + 1e-30
+        assert (err <= bound).all(), f"{(err > bound).sum()} gradient mismatches"
