@@ -63,3 +63,19 @@ def test_backward_sweep(T, E, k, m, cf, renorm):
         err = np.abs(dl.astype(np.float64) - ref)
         bound = 1e-5 * np.maximum(np.abs(ref), scale) + 1e-30
         assert (err <= bound).all(), f"{(err > bound).sum()} gradient mismatches"
+
+
+@pytest.mark.parametrize("T,E,k,m,cf,renorm", _cases(10, seed=314),
+                         ids=[f"T{c[0]}_E{c[1]}_k{c[2]}_m{c[3]}" for c in _cases(10, seed=314)])
+def test_select_bias_sweep(T, E, k, m, cf, renorm):
+    """Loss-free balancing: experts ranked by the fp32 sum of logit and
+    selection bias (the bias row kernels), weights and statistics unbiased."""
+    print(f"case bias sweep T={T} E={E} k={k} m={m}", flush=True)
+    rng = np.random.default_rng(T * 5 + E)
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    b = rng.normal(0.0, 0.5, E).astype(np.float32)
+    p = lbs.make_params(T, E, k, n_micro=m, capacity_factor=cf, renorm=renorm,
+                        save_row_stats=True, inv_perm=True, select_bias=True)
+    g = gpu_forward(p, {"logits": L, "select_bias": b})
+    r = oracle_forward(p, L, select_bias=b)
+    compare_forward(g, r, p)
