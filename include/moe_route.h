@@ -72,8 +72,9 @@ typedef struct {
     int32_t  T, E, k, n_micro; /* 1 <= k <= E <= MOE_ROUTE_MAX_E, k <= MOE_ROUTE_MAX_K,
                                   T % n_micro == 0, T*k < 2^31 */
     int32_t  d;                /* 0: logits are given; > 0: gate path, logits = X[T,d].Wg[d,E] */
-    float    capacity_factor;  /* used when capacity < 0; <= 0 means no limit */
     int32_t  capacity;         /* >= 0: per-microbatch capacity C; -1: from capacity_factor */
+    double   capacity_factor;  /* used when capacity < 0; <= 0 means no limit (see
+                                  moe_route_capacity for how it is rounded) */
     float    alpha;            /* aux-loss weight; 0 is legal (aux = 0, gradient = 0) */
     uint32_t flags;            /* MOE_* flags above */
 } moe_route_params;
@@ -145,9 +146,16 @@ int moe_route_workspace_size(const moe_route_params *p, size_t *bytes);
 
 /*
  * Per-microbatch capacity C for these parameters (host only, no device
- * work): C = ceil(cf * ceil(Tm*k/E)) from [p1] 4.5 with the k picks of a
- * token counted as k assignments; -1 when unlimited; the explicit capacity
- * field wins when >= 0.
+ * work).  [p1] 4.5 sets the capacity to the per-expert share of the batch,
+ * rounded up, times the capacity factor (1024 tokens, 8 experts, 1.25 ->
+ * 160); the k picks of a token count as k assignments, and a fractional
+ * product is rounded up:  C = ceil(cf * n),  n = ceil(Tm*k/E).
+ * The factor is the decimal the caller means (1.1, 1.2, ...), which a
+ * double holds only to within half an ulp, so a product within 2^-50
+ * (relative) of an integer is that integer: 1.1 * 50 gives 55 although the
+ * double product is 55.000000000000007.  Exact for factors with at most
+ * five decimal places.  -1 when unlimited (cf <= 0); the explicit capacity
+ * field wins when >= 0; results above INT32_MAX are clamped to it.
  */
 int moe_route_capacity(const moe_route_params *p, int32_t *capacity);
 

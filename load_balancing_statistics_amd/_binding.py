@@ -41,8 +41,8 @@ class MoeRouteError(RuntimeError):
 
 class moe_route_params(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
-                ("n_micro", ctypes.c_int32), ("d", ctypes.c_int32),
-                ("capacity_factor", ctypes.c_float), ("capacity", ctypes.c_int32),
+                ("n_micro", ctypes.c_int32), ("d", ctypes.c_int32), ("capacity", ctypes.c_int32),
+                ("capacity_factor", ctypes.c_double),
                 ("alpha", ctypes.c_float), ("flags", ctypes.c_uint32)]
 
 
@@ -106,8 +106,8 @@ def make_params(T, E, k, n_micro=1, d=0, capacity_factor=1.0, capacity=-1, alpha
     flags = ((MOE_RENORM_TOPK if renorm else 0) | (MOE_SAVE_ROW_STATS if save_row_stats else 0)
              | (MOE_WRITE_INV_PERM if inv_perm else 0) | (MOE_SELECT_BIAS if select_bias else 0)
              | (MOE_P_MASKED if p_masked else 0))
-    return moe_route_params(int(T), int(E), int(k), int(n_micro), int(d), float(capacity_factor),
-                            int(capacity), float(alpha), flags)
+    return moe_route_params(int(T), int(E), int(k), int(n_micro), int(d), int(capacity),
+                            float(capacity_factor), float(alpha), flags)
 
 
 def _ptr(t):

@@ -30,8 +30,7 @@ int check_shape(const moe_route_params* p) {
     if (p->d > 0 && !moe::gate_supported(p->T, p->d, p->E)) return MOE_ERR_UNSUPPORTED;
     const bool bias = (p->flags & MOE_SELECT_BIAS) != 0;
     const RowCfg c = moe::choose_rows(p->T, p->E, p->k, p->n_micro, bias);
-    const bool masked = (p->flags & MOE_P_MASKED) != 0;
-    if (c.G < 0 || moe::rows_lds_bytes(c, p->E, p->k, bias, masked) > kMaxLds) return MOE_ERR_UNSUPPORTED;
+    if (c.G < 0 || moe::rows_lds_bytes(c, p->E, p->k, bias) > kMaxLds) return MOE_ERR_UNSUPPORTED;
     if (moe::scatter_lds_bytes(p->E, p->k, moe::scatter_waves(p->E, c.NW)) > kMaxLds) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
@@ -40,12 +39,23 @@ RowCfg cfg_of(const moe_route_params* p) {
     return moe::choose_rows(p->T, p->E, p->k, p->n_micro, (p->flags & MOE_SELECT_BIAS) != 0);
 }
 
+// Capacity of page mhpq.cn/news/998159 section 4.5: the per-expert share of
+// a microbatch's Tm*k assignments, rounded up, times the capacity factor,
+// rounded up.  The factor is the decimal the caller writes (1.1, 1.2, ...),
+// which a double holds to within half an ulp; the product takes that error
+// and its own rounding (together under 2^-52 relative), so a product within
+// 2^-50 of an integer is that integer -- 1.1 * 50 is 55 although the double
+// product is 55.000000000000007 -- and any other product is rounded up.  A
+// factor with at most five decimal places and a product below 2^31 always
+// keeps a fractional part of at least 1e-5, far outside that window.
 int64_t capacity_of(const moe_route_params* p) {
     if (p->capacity >= 0) return p->capacity;
-    if (!(p->capacity_factor > 0.f)) return -1;
+    if (!(p->capacity_factor > 0.0)) return -1;
     const int64_t Tm = p->T / p->n_micro;
     const int64_t per_expert = (Tm * p->k + p->E - 1) / p->E;
-    const double c = std::ceil(double(p->capacity_factor) * double(per_expert));
+    const double x = p->capacity_factor * double(per_expert);
+    const double r = std::nearbyint(x);
+    const double c = (std::fabs(x - r) <= x * 0x1p-50) ? r : std::ceil(x);
     return c > double(INT_MAX) ? INT_MAX : int64_t(c);
 }
 

@@ -42,15 +42,17 @@ inline int next_pow2(int v) {
 }
 
 // Pick the lane mapping: the narrowest segment (S >= k, power of two) whose
-// per-lane column count fits the table.  Then the waves per block and the
-// rows per block: one or two resident blocks per compute unit over the whole
-// batch, so the grid is one wave of blocks and the per-block partials stay
-// few.
+// per-lane column count fits the table; a single lane per row takes at most
+// 8 columns (with one lane per row a wave keeps 64 rows' candidate lists and
+// row copies in LDS, which at 16 or 24 columns do not fit).  Then the waves
+// per block and the rows per block: one or two resident blocks per compute
+// unit over the whole batch, so the grid is one wave of blocks and the
+// per-block partials stay few.
 inline RowCfg choose_rows(int T, int E, int k, int n_micro, bool bias = false) {
     RowCfg c{};
     c.VEC = (E % 4 == 0) ? 4 : 1;
     int S = next_pow2(k < 1 ? 1 : k);
-    while (S < 64 && (E + S - 1) / S > kGMax) S <<= 1;
+    while (S < 64 && ((E + S - 1) / S > kGMax || (S == 1 && E > 8))) S <<= 1;
     c.S = S;
     const int g0 = (E + S - 1) / S;
     c.G = -1;
@@ -126,9 +128,9 @@ inline int rows_queue_cap(const RowCfg& c) {
     return ((c.R + per_iter - 1) / per_iter) * W;
 }
 
-inline size_t rows_lds_bytes(const RowCfg& c, int E, int k, bool bias = false, bool masked = false) {
+inline size_t rows_lds_bytes(const RowCfg& c, int E, int k, bool bias = false) {
     const int W = 64 / c.S;
-    size_t hist = align_up(size_t(E) * 4, 16) * (bias ? 2 : 1) + (masked ? align_up(size_t(E) * 8, 16) : 0);
+    size_t hist = align_up(size_t(E) * 4, 16) * (bias ? 2 : 1);
     size_t rowbuf = size_t(c.NW) * W * row_stride(c.S, c.G) * 4;
     size_t cand = size_t(c.NW) * W * cand_stride(c.S, c.G) * 8;
     size_t sel = size_t(c.NW) * W * k * 8;
@@ -184,7 +186,7 @@ struct RowsArgs {
     const float* bias;  // [E] selection bias, or nullptr
     int T, E, k, Tm, R, bpm;
     int renorm, save_stats;
-    int p_masked;  // P from the picks only (divided by Tm*k later)
+    int p_masked;  // P from the picks only (divided by Tm*k by the scatter)
     int qcap;  // per-wave queue entries: row groups of the largest block times rows per group
     int32_t* topk_idx;
     float* topk_w;

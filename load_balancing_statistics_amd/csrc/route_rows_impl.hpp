@@ -141,11 +141,14 @@ __device__ __forceinline__ void load_row(float (&x)[G], const float* __restrict_
     }
 }
 
-// A probability of a picked expert as a 2^-32 fixed-point integer: masked
-// probability sums are accumulated with integer LDS atomics, so their value
-// does not depend on the order of the additions.
-__device__ __forceinline__ unsigned long long prob_fixed(float p) {
-    return (p > 0.f) ? (unsigned long long)(double(p) * 4294967296.0 + 0.5) : 0ull;
+// Masked P sums (page mhpq.cn/news/998159 section 4.4's top-k form: only a
+// token's picks count) are accumulated like the all-token sums -- per-lane
+// fp32 in row order, then fixed-order combines -- so they keep fp32's
+// relative precision however small a pick's probability is.  A column is
+// picked when its selection key is at least the row's k-th key: larger
+// value, or equal value (-0.0 == +0.0) and a column no higher.
+__device__ __forceinline__ bool picked_col(float y, int col, float kv, int kc) {
+    return y > kv || (y == kv && col <= kc);
 }
 
 template <int S, int G, int VEC, bool PAD, int NW, bool BIAS>
@@ -158,7 +161,7 @@ struct RowPass {
 
     // Exact top-k of a row from its LDS copy: k rounds of arg-max of the
     // order keys over the segment (rows whose candidate list overflows).
-    __device__ __forceinline__ static void fallback_select(
+    __device__ __forceinline__ static uint64_t fallback_select(
         const float* rowbuf, const float* blds, uint64_t* sel, int E, int k, int s) {
         uint64_t prev = ~0ull;
         for (int j = 0; j < k; ++j) {
@@ -175,6 +178,7 @@ struct RowPass {
             if (s == 0) sel[j] = best;
             prev = best;
         }
+        return prev;  // the k-th key (segment-uniform)
     }
 
     __device__ __forceinline__ static int col_from_bit(int g, int s) {
@@ -192,7 +196,7 @@ struct RowPass {
         const RowsArgs& a, const float (&x)[G], long row, bool valid, int s,
         float* rowbuf, uint64_t* cand, int* hist, float (&acc)[G], int& bad,
         int* queue, int& qn, long row_begin, const float (&bz)[G], const float* blds,
-        unsigned long long* pm)
+        uint64_t* sel)
     {
         const int E = a.E, k = a.k;
         // ---- row maximum (softmax) and the candidate threshold tau
@@ -338,6 +342,28 @@ struct RowPass {
                         wcol[p] = key_col(my);
                         const float lv = BIAS ? rowbuf[wcol[p]] : key_val(my);
                         we[p] = __builtin_amdgcn_exp2f(fmaf(lv, kLog2e, -mL));
+                        if (rank == k - 1) sel[0] = my;  // the k-th key, for masked P
+                    }
+                }
+            }
+            if (a.p_masked) {
+                // masked P: each owner adds the probabilities of its picked
+                // columns (recomputed here, so the all-token path keeps ex[]
+                // short-lived)
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                const uint64_t kth = sel[0];
+                const float kv = key_val(kth);
+                const int kc = key_col(kth);
+                if (valid) {
+#pragma unroll
+                    for (int g = 0; g < G; ++g) {
+                        const int col = col_of<S, VEC>(g, s);
+                        const float y = BIAS ? x[g] + bz[g] : x[g];
+                        const float pv = __builtin_amdgcn_exp2f(fmaf(x[g], kLog2e, -mL));
+                        const bool pk = (!PAD || col < E) && picked_col(y, col, kv, kc);
+                        acc[g] = pk ? fmaf(pv, inv, acc[g]) : acc[g];
                     }
                 }
             }
@@ -355,7 +381,6 @@ struct RowPass {
                     a.topk_idx[row * k + wrank[p]] = wcol[p];
                     a.topk_w[row * k + wrank[p]] = we[p] * rden;
                     atomicAdd(&hist[wcol[p]], 1);
-                    if (a.p_masked) atomicAdd(&pm[wcol[p]], prob_fixed(we[p] * inv));
                 }
             }
             if (s == 0 && a.save_stats) {
@@ -366,11 +391,12 @@ struct RowPass {
     }
 
     // Queued rows (candidate-list overflow): reload, softmax statistics, exact
-    // top-k by k rounds of arg-max, outputs.  Probability sums were already
-    // accumulated by the streaming pass.
+    // top-k by k rounds of arg-max, outputs.  The all-token probability sums
+    // were already accumulated by the streaming pass; the masked ones, which
+    // need the picks, are added here.
     __device__ __forceinline__ static void resolve_queue(
         const RowsArgs& a, const int* queue, int qn, long row_begin, int s, int seg,
-        float* rowbuf, uint64_t* sel, int* hist, const float* blds, unsigned long long* pm)
+        float* rowbuf, uint64_t* sel, int* hist, const float* blds, float (&acc)[G])
     {
         const int E = a.E, k = a.k;
         for (int q0 = 0; q0 < qn; q0 += W) {
@@ -389,7 +415,19 @@ struct RowPass {
             ssum = seg_sum<S>(ssum);
 #pragma unroll
             for (int g = 0; g < G; ++g) rowbuf[col_of<S, VEC>(g, s)] = x[g];
-            fallback_select(rowbuf, blds, sel, E, k, s);
+            const uint64_t kth = fallback_select(rowbuf, blds, sel, E, k, s);
+            if (a.p_masked && has) {
+                const float kv = key_val(kth), inv = __builtin_amdgcn_rcpf(ssum);
+                const int kc = key_col(kth);
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const int col = col_of<S, VEC>(g, s);
+                    const float y = BIAS ? x[g] + ((!PAD || col < E) ? blds[col] : 0.f) : x[g];
+                    const float pv = __builtin_amdgcn_exp2f(fmaf(x[g], kLog2e, -mL));
+                    const bool pk = (!PAD || col < E) && picked_col(y, col, kv, kc);
+                    acc[g] = pk ? fmaf(pv, inv, acc[g]) : acc[g];
+                }
+            }
             float e = 0.f;
             int col = 0;
             if (s < k) {
@@ -404,7 +442,6 @@ struct RowPass {
                 a.topk_idx[row * k + s] = col;
                 a.topk_w[row * k + s] = e * rden;
                 atomicAdd(&hist[col], 1);
-                if (a.p_masked) atomicAdd(&pm[col], prob_fixed(e * __builtin_amdgcn_rcpf(ssum)));
             }
         }
     }
@@ -427,10 +464,8 @@ route_rows_kernel(const RowsArgs a)
     const int E = a.E, k = a.k;
     int* hist = reinterpret_cast<int*>(smem);
     float* blds = reinterpret_cast<float*>(smem + ((E * 4 + 15) & ~15));  // [E] when BIAS
-    unsigned long long* pm = reinterpret_cast<unsigned long long*>(
-        reinterpret_cast<unsigned char*>(blds) + (BIAS ? ((E * 4 + 15) & ~15) : 0));  // [E] when masked
     float* rowbuf_all = reinterpret_cast<float*>(
-        reinterpret_cast<unsigned char*>(pm) + (a.p_masked ? ((E * 8 + 15) & ~15) : 0));
+        reinterpret_cast<unsigned char*>(blds) + (BIAS ? ((E * 4 + 15) & ~15) : 0));
     uint64_t* cand_all = reinterpret_cast<uint64_t*>(
         reinterpret_cast<unsigned char*>(rowbuf_all) + ((NW * W * RS * 4 + 15) & ~15));
     uint64_t* sel_all = cand_all + NW * W * CS;
@@ -446,8 +481,6 @@ route_rows_kernel(const RowsArgs a)
     if (a.status && blockIdx.x == 0 && tid == 0) a.status[0] = 0;
     if constexpr (BIAS)
         for (int e = tid; e < E; e += NW * 64) blds[e] = a.bias[e];
-    if (a.p_masked)
-        for (int e = tid; e < E; e += NW * 64) pm[e] = 0ull;
     __syncthreads();
 
     float* rowbuf = rowbuf_all + (wave * W + seg) * RS;
@@ -486,22 +519,22 @@ route_rows_kernel(const RowsArgs a)
     int it = 0;
     for (; it + 2 < iters; it += 2) {
         load_row<S, G, VEC, PAD>(xb, a.logits, clamp(row_at(it + 1)), E, s);
-        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin, bz, blds, pm);
+        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin, bz, blds, sel);
         load_row<S, G, VEC, PAD>(xa, a.logits, clamp(row_at(it + 2)), E, s);
         RP::process(a, xb, row_at(it + 1), row_at(it + 1) < row_end, s, rowbuf, cand, hist,
-                    acc, bad, queue, qn, row_begin, bz, blds, pm);
+                    acc, bad, queue, qn, row_begin, bz, blds, sel);
     }
     if (it + 1 < iters) {
         load_row<S, G, VEC, PAD>(xb, a.logits, clamp(row_at(it + 1)), E, s);
-        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin, bz, blds, pm);
+        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin, bz, blds, sel);
         RP::process(a, xb, row_at(it + 1), row_at(it + 1) < row_end, s, rowbuf, cand, hist,
-                    acc, bad, queue, qn, row_begin, bz, blds, pm);
+                    acc, bad, queue, qn, row_begin, bz, blds, sel);
     } else if (it < iters) {
-        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin, bz, blds, pm);
+        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin, bz, blds, sel);
     }
 
     if (__builtin_expect(qn > 0, 0))
-        RP::resolve_queue(a, queue, qn, row_begin, s, seg, rowbuf, sel, hist, blds, pm);
+        RP::resolve_queue(a, queue, qn, row_begin, s, seg, rowbuf, sel, hist, blds, acc);
 
     // ---- block partials: probability sums (fixed order) and histogram.
     // Lanes with the same s in different segments own the same columns.
@@ -527,12 +560,8 @@ route_rows_kernel(const RowsArgs a)
     const long bo = long(blockIdx.x) * E;
     for (int e = tid; e < E; e += NW * 64) {
         float t = 0.f;
-        if (a.p_masked) {
-            t = float(double(pm[e]) * 0x1p-32);
-        } else {
 #pragma unroll
-            for (int w = 0; w < NW; ++w) t += pbuf[w * E + e];
-        }
+        for (int w = 0; w < NW; ++w) t += pbuf[w * E + e];
         a.P_part[bo + e] = t;
         a.cnt_part[bo + e] = hist[e];
     }
@@ -714,7 +743,7 @@ route_backward_kernel(const BackArgs a)
 
 template <int S, int G, int VEC, bool PAD, int NW, bool BIAS>
 hipError_t launch_rows_nw(const RowCfg& c, const RowsArgs& a, hipStream_t st) {
-    const size_t lds = rows_lds_bytes(c, a.E, a.k, BIAS, a.p_masked != 0);
+    const size_t lds = rows_lds_bytes(c, a.E, a.k, BIAS);
     auto kern = route_rows_kernel<S, G, VEC, PAD, NW, BIAS>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),

@@ -53,19 +53,75 @@ static double bf16_to_double(uint16_t h)
  * expert share of the batch, rounded up, times the capacity factor; its
  * worked example is 1024 tokens, 8 experts, factor 1.25 -> 160.
  * Reading for top-k (k assignments per token): the load to spread is Tm*k
- * assignments, and the product with the factor is rounded up:
+ * assignments, and a fractional product with the factor is rounded up:
  *   C = ceil(cf * ceil(Tm*k / E)).
+ * The factor is the decimal number the caller wrote ("1.1", "1.25",
+ * "5e-1"), taken as text so that it is exact: cf = M * 10^-D with integer
+ * M, and the product is formed and rounded up in integer arithmetic, so an
+ * integral product stays integral (1.1 * 50 = 55).
  * cf <= 0 means "no limit" (returned as -1).  A non-negative override wins.
+ * A capacity above 2^31 - 1 (more than any call's assignments) is returned
+ * as 2^31 - 1.  Returns -2 when the text is not a decimal number.
  */
-long long oracle_capacity(long long Tm, long long E, long long k, double cf,
+long long oracle_capacity(long long Tm, long long E, long long k, const char *cf_text,
                           long long capacity_override)
 {
+    const long long cap_max = 2147483647LL;
     if (capacity_override >= 0)
         return capacity_override;
-    if (!(cf > 0.0))
+    /* parse [+|-]digits[.digits][(e|E)[+|-]digits] into M and D */
+    const char *c = cf_text;
+    int neg = 0, digits = 0, frac = 0, seen_dot = 0;
+    unsigned __int128 M = 0;
+    if (*c == '+' || *c == '-')
+        neg = (*c++ == '-');
+    for (; *c; ++c) {
+        if (*c == '.' && !seen_dot) {
+            seen_dot = 1;
+        } else if (*c >= '0' && *c <= '9') {
+            if (M > (((unsigned __int128)1) << 100))
+                return -2; /* more digits than any double's decimal form */
+            M = M * 10 + (unsigned)(*c - '0');
+            frac += seen_dot;
+            ++digits;
+        } else {
+            break;
+        }
+    }
+    long long ex = 0;
+    if (*c == 'e' || *c == 'E') {
+        ++c;
+        int eneg = 0;
+        if (*c == '+' || *c == '-')
+            eneg = (*c++ == '-');
+        if (!(*c >= '0' && *c <= '9'))
+            return -2;
+        for (; *c >= '0' && *c <= '9'; ++c)
+            if (ex < 100000)
+                ex = ex * 10 + (*c - '0');
+        ex = eneg ? -ex : ex;
+    }
+    if (*c != '\0' || digits == 0)
+        return -2;
+    if (neg || M == 0)
         return -1;
+    long long D = frac - ex; /* cf = M * 10^-D */
     long long per_expert = (Tm * k + E - 1) / E; /* ceil(Tm*k/E) */
-    return (long long)ceil(cf * (double)per_expert);
+    unsigned __int128 num = M * (unsigned __int128)per_expert;
+    unsigned __int128 cap;
+    if (D <= 0) {
+        cap = num;
+        for (long long i = 0; i < -D && cap <= (unsigned __int128)cap_max; ++i)
+            cap *= 10;
+    } else if (D > 38) {
+        cap = (num > 0) ? 1 : 0; /* 0 < cf * n < 1 */
+    } else {
+        unsigned __int128 den = 1;
+        for (long long i = 0; i < D; ++i)
+            den *= 10;
+        cap = (num + den - 1) / den;
+    }
+    return cap > (unsigned __int128)cap_max ? cap_max : (long long)cap;
 }
 
 /*

@@ -23,7 +23,7 @@ def load_library(path=None):
         _build.build(out=p)
     lib = ctypes.CDLL(p)
     ll, d, vp, i = ctypes.c_longlong, ctypes.c_double, ctypes.c_void_p, ctypes.c_int
-    lib.oracle_capacity.argtypes = [ll, ll, ll, d, ll]
+    lib.oracle_capacity.argtypes = [ll, ll, ll, ctypes.c_char_p, ll]
     lib.oracle_capacity.restype = ll
     lib.oracle_gate_logits.argtypes = [vp, vp, ll, ll, ll, vp]
     lib.oracle_gate_logits.restype = None
@@ -49,10 +49,18 @@ def _p(a):
 
 
 def capacity(Tm, E, k, capacity_factor, capacity_override=-1, lib=None):
-    """Per-microbatch capacity C (``-1`` = unlimited)."""
+    """Per-microbatch capacity C (``-1`` = unlimited).
+
+    ``capacity_factor`` is the caller's number: a string is used as written,
+    a float as the shortest decimal that reads back as that float (its
+    ``repr``: 1.1 -> "1.1"), so the oracle computes with the decimal the
+    caller typed, exactly."""
     lib = lib or load_library()
-    return int(lib.oracle_capacity(int(Tm), int(E), int(k), float(capacity_factor),
-                                   int(capacity_override)))
+    text = capacity_factor if isinstance(capacity_factor, str) else repr(float(capacity_factor))
+    C = int(lib.oracle_capacity(int(Tm), int(E), int(k), text.encode(), int(capacity_override)))
+    if C < -1:
+        raise ValueError(f"capacity factor {text!r} is not a decimal number")
+    return C
 
 
 def gate_logits(X_bits, Wg_bits, lib=None):

@@ -56,12 +56,17 @@ def gpu_backward(params, logits, counts, row_stats=None, d_aux=None):
     return dl.cpu().numpy()
 
 
-def oracle_forward(params, logits, select_bias=None):
+def oracle_forward(params, logits, select_bias=None, capacity_factor=None):
+    """The oracle on the same logits; ``capacity_factor`` is the caller's
+    number (a float or a decimal string), by default the float the params
+    carry (a double: the caller's float unchanged)."""
     cap = params.capacity
+    cf = params.capacity_factor if capacity_factor is None else capacity_factor
     return oracle.route(logits, params.k, n_micro=params.n_micro,
-                        capacity_factor=params.capacity_factor, capacity_override=cap,
+                        capacity_factor=cf, capacity_override=cap,
                         alpha=params.alpha, renorm=bool(params.flags & lbs.MOE_RENORM_TOPK),
-                        select_bias=select_bias)
+                        select_bias=select_bias,
+                        p_masked=bool(params.flags & lbs.MOE_P_MASKED))
 
 
 def assert_close_rel(got, ref, rtol, atol=0.0, what=""):
@@ -126,9 +131,14 @@ def backward_tolerance(logits, r, counts, params, d_aux=None):
 
 def check_structure(g, params):
     """Properties that hold for any valid routing output (used where several
-    selections are correct, e.g. near-ties of the bf16 gate logits)."""
+    selections are correct, e.g. near-ties of the bf16 gate logits): counts
+    are the histogram of the picks, offsets their prefix, perm the stable
+    expert sort, inv_perm its inverse, and an assignment is dropped exactly
+    when it sits C or more places past its expert's offset (C from the
+    oracle's capacity)."""
     T, E, k, m = params.T, params.E, params.k, params.n_micro
     Tm = T // m
+    C = oracle.capacity(Tm, E, k, params.capacity_factor, params.capacity)
     idx = g["topk_idx"].reshape(m, Tm * k)
     for mb in range(m):
         cnt = np.bincount(idx[mb], minlength=E)
@@ -136,5 +146,10 @@ def check_structure(g, params):
         assert np.array_equal(g["offsets"][mb], np.concatenate([[0], np.cumsum(cnt)]))
         seg = g["perm"][mb * Tm * k:(mb + 1) * Tm * k]
         assert np.array_equal(seg, np.argsort(idx[mb], kind="stable") + mb * Tm * k)
+        # place of each assignment inside its expert's run
+        e_sorted = idx[mb][seg - mb * Tm * k]
+        rank = np.arange(Tm * k) - g["offsets"][mb][e_sorted]
+        want = (rank >= C) if C >= 0 else np.zeros(Tm * k, bool)
+        assert np.array_equal(g["dropped"][seg].astype(bool), want), "dropped"
     assert np.array_equal(g["inv_perm"][g["perm"]], np.arange(T * k))
     assert (np.sort(g["topk_idx"], axis=1)[:, 1:] != np.sort(g["topk_idx"], axis=1)[:, :-1]).all()

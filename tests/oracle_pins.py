@@ -72,6 +72,29 @@ def pin_capacity_worked_example(lib):
     assert np.array_equal(dropped_per_e.astype(np.int64), np.maximum(counts - C, 0))
 
 
+def pin_capacity_recommended_factors(lib):
+    """[p1] 4.5 at the factors the page recommends (1.0-1.05 late, 1.2-1.5
+    early): the product is the decimal the caller wrote times the rounded-up
+    share, and an integral product stays integral (1280 tokens, 128 experts,
+    1.2 -> 12; 5000 tokens, 100 experts, 1.1 -> 55).  The values were worked
+    by hand (``tests/golden/capacity_factors.txt``); the same factors given
+    as the caller's float and as text give the same capacity."""
+    rows = []
+    with open(os.path.join(GOLDEN, "capacity_factors.txt")) as fh:
+        for line in fh:
+            if line.strip() and not line.startswith("#"):
+                rows.append(dict(tok.split("=") for tok in line.split()))
+    assert len(rows) >= 10
+    for r in rows:
+        T, E, k, C = int(r["tokens"]), int(r["experts"]), int(r["top_k"]), int(r["capacity"])
+        assert oracle.capacity(T, E, k, float(r["capacity_factor"]), lib=lib) == C, r
+        assert oracle.capacity(T, E, k, r["capacity_factor"], lib=lib) == C, r
+    # factor 1 is the share itself; a factor of one half rounds the half up
+    assert oracle.capacity(999, 10, 1, 1.0, lib=lib) == 100
+    assert oracle.capacity(990, 10, 1, "5e-1", lib=lib) == 50
+    assert oracle.capacity(1000, 10, 1, 0.505, lib=lib) == 51
+
+
 def pin_balanced_routing_drops_nothing(lib):
     """[p1] 4.5 recommends factors near 1.0 for peak efficiency, which only
     makes sense if perfectly balanced routing at factor 1.0 drops nothing.

@@ -85,6 +85,61 @@ def test_capacity_and_workspace(lbs):
         assert 0 < n < 64 * 1024 * 1024
 
 
+def test_capacity_at_recommended_factors(lbs):
+    """The library's capacity equals the page's formula (mhpq.cn/news/998159
+    section 4.5) at the factors the page recommends, as worked by hand in
+    tests/golden/capacity_factors.txt: 1280 tokens over 128 experts at 1.2 is
+    12, 5000 over 100 at 1.1 is 55 (the double product 55.000000000000007
+    must not round up to 56)."""
+    path = os.path.join(ROOT, "tests", "golden", "capacity_factors.txt")
+    n = 0
+    for line in open(path):
+        if not line.strip() or line.startswith("#"):
+            continue
+        r = dict(tok.split("=") for tok in line.split())
+        T, E, k = int(r["tokens"]), int(r["experts"]), int(r["top_k"])
+        p = lbs.make_params(T, E, k, capacity_factor=float(r["capacity_factor"]))
+        assert lbs.moe_route_capacity(p) == int(r["capacity"]), r
+        n += 1
+    assert n >= 10
+
+
+def test_capacity_matches_oracle_over_decimal_factors(lbs):
+    """Library (double factor, products within 2^-50 of an integer taken as
+    that integer) against the oracle (the caller's decimal, exact integer
+    arithmetic) over factors with one to four decimal places and per-expert
+    shares from 1 to 5000, microbatches and k > 1 included."""
+    import numpy as np
+    import oracle
+    rng = np.random.default_rng(7)
+    factors = sorted({round(x, d) for d in (1, 2, 3, 4)
+                      for x in rng.uniform(0.05, 4.0, size=60)} | {1.05, 1.1, 1.15, 1.2, 1.3, 1.5})
+    shapes = [(T, E, k, m) for T, E, k, m in [(1, 1, 1, 1), (4096, 8, 1, 1), (65536, 64, 2, 1),
+                                               (131072, 256, 8, 1), (262144, 384, 6, 16),
+                                               (5000, 100, 1, 1), (3000, 7, 3, 3)]]
+    shapes += [(int(s) * 10, 10, 1, 1) for s in rng.integers(1, 5000, size=40)]
+    for cf in factors:
+        for T, E, k, m in shapes:
+            p = lbs.make_params(T, E, k, n_micro=m, capacity_factor=cf)
+            want = oracle.capacity(T // m, E, k, cf)
+            assert lbs.moe_route_capacity(p) == want, (cf, T, E, k, m)
+
+
+def test_every_expert_count_and_k_is_supported(lbs):
+    """Every E <= MOE_ROUTE_MAX_E and k <= min(E, MOE_ROUTE_MAX_K) is accepted,
+    with and without the selection bias and the masked P (top-1 over 9 to 24
+    experts once overflowed the row pass's LDS)."""
+    for flags in [dict(), dict(select_bias=True, p_masked=True)]:
+        bad = []
+        for E in range(1, lbs.MOE_ROUTE_MAX_E + 1):
+            for k in range(1, min(E, lbs.MOE_ROUTE_MAX_K) + 1):
+                try:
+                    lbs.moe_route_workspace_size(lbs.make_params(100000, E, k, **flags))
+                except lbs.MoeRouteError:
+                    bad.append((E, k))
+        assert not bad, (flags, bad[:10])
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(T=0, E=8, k=1), -1), (dict(T=16, E=8, k=0), -1), (dict(T=16, E=8, k=9), -1),
     (dict(T=15, E=8, k=1, n_micro=2), -1), (dict(T=16, E=2048, k=2), -2),

@@ -149,3 +149,28 @@ def test_grad_full_v4_masked_weights():
     r = oracle.route(inp["logits"], w.k, n_micro=w.n_micro, capacity_factor=w.capacity_factor,
                      alpha=w.alpha, renorm=w.renorm, p_masked=True)
     _check_grad(inp["logits"], w, p, g, r, True, w.renorm, True, use_stats=True, seed=7)
+
+
+@pytest.mark.parametrize("T,E,k,m,kind", [(4000, 384, 6, 2, "wide"), (3001, 256, 8, 1, "hot"),
+                                          (2500, 64, 4, 1, "hot")])
+def test_masked_P_peaked_logits(T, E, k, m, kind):
+    """Masked P where picked probabilities span many orders of magnitude:
+    router logits N(0, 8^2) ("wide"), or three experts boosted by +30 so that
+    every token's remaining picks carry probabilities near 1e-13 ("hot").
+    Experts picked only as a low choice then have a tiny P, which must still
+    match the oracle within 1e-5 relative."""
+    print(f"case masked_P_peaked T={T} E={E} k={k} m={m} kind={kind}", flush=True)
+    rng = np.random.default_rng(T + E)
+    if kind == "wide":
+        L = (8.0 * rng.standard_normal((T, E))).astype(np.float32)
+    else:
+        L = rng.standard_normal((T, E)).astype(np.float32)
+        L[:, rng.choice(E, 3, replace=False)] += 30.0
+    p = lbs.make_params(T, E, k, n_micro=m, capacity_factor=1.0, alpha=0.01, renorm=True,
+                        save_row_stats=True, inv_perm=True, p_masked=True)
+    g = gpu_forward(p, {"logits": L})
+    r = oracle.route(L, k, n_micro=m, capacity_factor=1.0, alpha=0.01, renorm=True, p_masked=True)
+    if kind == "hot":
+        Pr = r["P"][r["P"] > 0]
+        assert Pr.min() < 1e-9 * Pr.max(), "the case must hold experts with tiny masked P"
+    compare_forward(g, r, p)

@@ -38,11 +38,12 @@ def test_forward_small(name, seed):
     compare_forward(g, r, p)
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("name", ["switch_top1", "zipf_top2", "v3_shape", "v4_shape"])
-def test_forward_full(name):
+def test_forward_full(name, seed):
     w = WORKLOADS[name]
-    print(f"case forward_full {name} T={w.T} E={w.E} k={w.k} m={w.n_micro}", flush=True)
-    inp = make_inputs(w, 0)
+    print(f"case forward_full {name} seed={seed} T={w.T} E={w.E} k={w.k} m={w.n_micro}", flush=True)
+    inp = make_inputs(w, seed)
     p = params_of(w)
     g = gpu_forward(p, inp)
     r = oracle_forward(p, inp["logits"])
@@ -74,10 +75,11 @@ def test_backward_small(name, use_stats):
     _check_backward(w, inp, p, g, r, d_aux=d_aux, use_stats=use_stats)
 
 
-def test_backward_full_v4():
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_backward_full_v4(seed):
     w = WORKLOADS["v4_shape"]
-    print("case backward_full v4_shape", flush=True)
-    inp = make_inputs(w, 0)
+    print(f"case backward_full v4_shape seed={seed}", flush=True)
+    inp = make_inputs(w, seed)
     p = params_of(w)
     g = gpu_forward(p, inp)
     r = oracle_forward(p, inp["logits"])
@@ -108,6 +110,10 @@ def _gate_case(w, seed):
     check_structure(g, p)
     if sure.all():
         compare_forward(g, r, p)
+    # every routing output bit-exact (floats 1e-5) against the oracle routing
+    # the very fp32 logits the gate GEMM wrote
+    rr = oracle_forward(params_of(w, d=0), g["logits"])
+    compare_forward(g, rr, p)
     # the routing behind the gate equals the routing of the logits it wrote
     p2 = params_of(w, d=0)
     g2 = gpu_forward(p2, {"logits": g["logits"]})
@@ -147,7 +153,8 @@ def test_gate_full():
     w = WORKLOADS["gate_top2"]
     print("case gate_full", flush=True)
     inp, p, g, r = _gate_case(w, 0)
-    # backward on the gate logits the forward wrote
+    # backward on the gate logits the forward wrote (the forward on them was
+    # compared with the oracle in _gate_case)
     rr = oracle_forward(params_of(w, d=0), g["logits"])
     ref = oracle.backward(g["logits"], w.k, rr["counts"], alpha=w.alpha)
     dl = gpu_backward(p, g["logits"], g["counts"], row_stats=g["row_stats"])
@@ -179,6 +186,13 @@ EDGE = [
     (700, 12, 5, 1, 1.0, -1, True, "quantized"),
     (2000, 250, 8, 1, 1.25, -1, True, "normal"),     # 16 lanes x 16 columns, scalar loads
     (3000, 130, 6, 2, 1.0, -1, False, "normal"),     # padded columns, two microbatches
+    # top-1 over 9..24 experts: two or four lanes per row
+    (3000, 9, 1, 1, 1.25, -1, False, "normal"),
+    (3001, 12, 1, 1, 1.1, -1, False, "normal"),
+    (4096, 16, 1, 2, 1.2, -1, False, "normal"),
+    (2500, 20, 1, 1, 1.05, -1, False, "normal"),
+    (2048, 24, 1, 1, 1.0, -1, False, "quantized"),
+    (1000, 13, 2, 1, 1.3, -1, True, "normal"),
 ]
 
 
@@ -209,6 +223,42 @@ def test_edge(case):
     compare_forward(g, r, p)
     if cap == 0:
         assert g["dropped"].all()
+
+
+# (tokens, experts, k, capacity factor as the caller writes it, capacity
+# worked by hand from page mhpq.cn/news/998159 section 4.5:
+# ceil(factor * ceil(tokens * k / experts)))
+RECOMMENDED_CF = [
+    (1280, 128, 1, "1.2", 12),
+    (5000, 100, 1, "1.1", 55),
+    (2000, 100, 1, "1.1", 22),
+    (640, 64, 2, "1.1", 22),
+    (3000, 100, 1, "1.05", 32),
+    (16384, 384, 6, "1.05", 269),
+]
+
+
+@pytest.mark.parametrize("case", RECOMMENDED_CF, ids=[f"T{c[0]}_E{c[1]}_k{c[2]}_cf{c[3]}"
+                                                      for c in RECOMMENDED_CF])
+def test_capacity_at_recommended_factors(case):
+    """Drops at the capacity factors the page recommends (1.0-1.05 late in
+    training, 1.2-1.5 early): the oracle is given the factor as the caller
+    wrote it (text), the library the caller's float; both must cut each
+    expert at the page's capacity, including where the product is integral
+    (1.2 * 10 = 12, 1.1 * 50 = 55)."""
+    T, E, k, cf_text, C = case
+    print(f"case capacity T={T} E={E} k={k} cf={cf_text}", flush=True)
+    rng = np.random.default_rng(T + E)
+    L = (rng.standard_normal((T, E)) + rng.normal(0.0, 0.3, E)).astype(np.float32)
+    p = lbs.make_params(T, E, k, capacity_factor=float(cf_text), alpha=0.01, renorm=k > 1,
+                        save_row_stats=True, inv_perm=True)
+    assert lbs.moe_route_capacity(p) == C
+    r = oracle_forward(p, L, capacity_factor=cf_text)
+    assert r["capacity"] == C
+    g = gpu_forward(p, {"logits": L})
+    assert (g["counts"] > C).any(), "the case must drop at the capacity"
+    compare_forward(g, r, p)
+    assert g["extra_stats"][0, 5] == C
 
 
 def test_alpha_zero_and_no_renorm():

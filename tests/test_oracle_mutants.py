@@ -34,6 +34,11 @@ MUTANTS = {
                            "long long per_expert = (Tm + E - 1) / E;"),
     "capacity_floor": ("long long per_expert = (Tm * k + E - 1) / E;",
                        "long long per_expert = (Tm * k) / E + (Tm * k) % 2;"),
+    "capacity_double_product": ("cap = (num + den - 1) / den;",
+                                "cap = (unsigned __int128)ceil(strtod(cf_text, NULL) * (double)per_expert);"),
+    "capacity_fp32_factor": ("cap = (num + den - 1) / den;",
+                             "cap = (unsigned __int128)ceil((double)strtof(cf_text, NULL) * (double)per_expert);"),
+    "capacity_product_truncated": ("cap = (num + den - 1) / den;", "cap = num / den;"),
     "drop_off_by_one": ("dropped[a] = (uint8_t)(capacity >= 0 && r >= capacity);",
                         "dropped[a] = (uint8_t)(capacity >= 0 && r > capacity);"),
     "perm_reversed_in_expert": ("long long pos = off[e] + r;",
