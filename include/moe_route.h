@@ -53,6 +53,8 @@ extern "C" {
 #define MOE_ERR_UNSUPPORTED (-2) /* E, k or gate shape beyond the limits      */
 #define MOE_ERR_WORKSPACE   (-3) /* workspace NULL or smaller than required   */
 #define MOE_ERR_HIP         (-4) /* a HIP launch or runtime call failed       */
+#define MOE_ERR_SCRATCH     (-5) /* moe_route_noalloc: the call needs more
+                                    than MOE_ROUTE_SCRATCH_BYTES of scratch   */
 
 /* moe_route_params.flags */
 #define MOE_RENORM_TOPK    1u /* rescale the k gate weights to sum to 1     */
@@ -176,6 +178,28 @@ int moe_route_capacity(const moe_route_params *p, int32_t *capacity);
 int moe_route(const moe_route_params *p, const float *logits, const uint16_t *X,
               const uint16_t *Wg, const float *select_bias, const moe_route_out *out,
               void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * moe_route for callers that cannot allocate device memory -- code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc: the
+ * same forward, with the workspace taken from a static device array of
+ * MOE_ROUTE_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * (from the first call there until the process ends).  The caller still
+ * passes the inputs and outputs, exactly as for moe_route; the call itself
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ * The scratch belongs to the device current on the calling thread, which
+ * must be the device of stream.  Every call on one GPU shares that GPU's
+ * scratch: calls that overlap on one GPU (other streams, other threads)
+ * race and must be ordered by the caller.  Nothing in the scratch needs to
+ * start at zero; it holds the last call's partials.
+ * Returns MOE_ERR_SCRATCH (nothing launched) when the shape needs more
+ * workspace than MOE_ROUTE_SCRATCH_BYTES (moe_route_workspace_size tells);
+ * otherwise the same codes as moe_route.
+ */
+#define MOE_ROUTE_SCRATCH_BYTES (32u * 1024u * 1024u)
+int moe_route_noalloc(const moe_route_params *p, const float *logits, const uint16_t *X,
+                      const uint16_t *Wg, const float *select_bias, const moe_route_out *out,
+                      void *stream);
 
 /*
  * One update of the selection bias after a forward ([p1] 4.3: an overloaded

@@ -16,6 +16,8 @@ MOE_ERR_INVALID_ARG = -1
 MOE_ERR_UNSUPPORTED = -2
 MOE_ERR_WORKSPACE = -3
 MOE_ERR_HIP = -4
+MOE_ERR_SCRATCH = -5
+MOE_ROUTE_SCRATCH_BYTES = 32 * 1024 * 1024
 
 MOE_RENORM_TOPK = 1
 MOE_SAVE_ROW_STATS = 2
@@ -80,6 +82,8 @@ def load(path=None):
     lib.moe_route_capacity.restype = ctypes.c_int
     lib.moe_route.argtypes = [P, vp, vp, vp, vp, ctypes.POINTER(moe_route_out), vp, ctypes.c_size_t, vp]
     lib.moe_route.restype = ctypes.c_int
+    lib.moe_route_noalloc.argtypes = [P, vp, vp, vp, vp, ctypes.POINTER(moe_route_out), vp]
+    lib.moe_route_noalloc.restype = ctypes.c_int
     lib.moe_route_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_route_backward.restype = ctypes.c_int
     lib.moe_route_bias_update.argtypes = [P, vp, ctypes.c_float, vp, vp]
@@ -160,6 +164,16 @@ def moe_route(params, out, workspace, logits=None, X=None, Wg=None, stream=None,
                           if workspace is not None else 0, _stream(stream))
     if rc != MOE_OK:
         raise MoeRouteError(rc, "moe_route")
+
+
+def moe_route_noalloc(params, out, logits=None, X=None, Wg=None, stream=None, select_bias=None):
+    """``moe_route`` with the library's static device scratch as workspace (no
+    allocation in the call); calls overlapping on one GPU race."""
+    o = moe_route_out(*[None if out.get(n) is None else out[n].data_ptr() for n in _OUT_FIELDS])
+    rc = load().moe_route_noalloc(ctypes.byref(params), _ptr(logits), _ptr(X), _ptr(Wg),
+                                  _ptr(select_bias), ctypes.byref(o), _stream(stream))
+    if rc != MOE_OK:
+        raise MoeRouteError(rc, "moe_route_noalloc")
 
 
 def moe_route_backward(params, logits, counts, dlogits, row_stats=None, d_aux=None,

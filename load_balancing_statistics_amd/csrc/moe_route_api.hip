@@ -5,8 +5,16 @@
 // for the forward, and the single streaming pass of the backward.
 #include <climits>
 #include <cmath>
+#include <mutex>
 
 #include "route_common.hpp"
+
+// Scratch of moe_route_noalloc: one call's workspace in a device array the
+// library owns.  The runtime gives every GPU that loads this library its own
+// copy at its own address.  In host code the name is only a stand-in, never
+// a device address: host code uses the per-device address that
+// hipGetSymbolAddress returns (scratch_of_current_device below).
+static __device__ __align__(256) unsigned char scratch[MOE_ROUTE_SCRATCH_BYTES];
 
 namespace {
 
@@ -62,6 +70,26 @@ int64_t capacity_of(const moe_route_params* p) {
 size_t workspace_bytes(const moe_route_params* p, const RowCfg& c) {
     const size_t gate = p->d > 0 ? moe::gate_workspace_bytes(p->d, p->E) : 0;
     return moe::carve_workspace(nullptr, c, p->E, p->n_micro, gate).bytes;
+}
+
+// Device address of the scratch array on the current device, looked up once
+// per device (the first moe_route_noalloc call there, with that device
+// current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+int scratch_of_current_device(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
 }
 
 }  // namespace
@@ -205,6 +233,18 @@ int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
     return MOE_OK;
 }
 
+int moe_route_noalloc(const moe_route_params* p, const float* logits, const uint16_t* X,
+                      const uint16_t* Wg, const float* select_bias, const moe_route_out* out,
+                      void* stream) {
+    const int rc = check_shape(p);
+    if (rc != MOE_OK) return rc;
+    if (workspace_bytes(p, cfg_of(p)) > size_t(MOE_ROUTE_SCRATCH_BYTES)) return MOE_ERR_SCRATCH;
+    void* ws = nullptr;
+    const int sc = scratch_of_current_device(&ws);
+    if (sc != MOE_OK) return sc;
+    return moe_route(p, logits, X, Wg, select_bias, out, ws, size_t(MOE_ROUTE_SCRATCH_BYTES), stream);
+}
+
 int moe_route_backward(const moe_route_params* p, const float* logits, const float* row_stats,
                        const int32_t* counts, const float* d_aux, const int32_t* topk_idx,
                        const float* d_topk_w, float* dlogits, void* stream) {
@@ -313,6 +353,8 @@ const char* moe_route_strerror(int code) {
         case MOE_ERR_UNSUPPORTED: return "unsupported shape (E, k, T*k or gate dimensions beyond the limits)";
         case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or smaller than moe_route_workspace_size()";
         case MOE_ERR_HIP: return "a HIP kernel launch failed";
+        case MOE_ERR_SCRATCH:
+            return "moe_route_noalloc: the shape needs more workspace than MOE_ROUTE_SCRATCH_BYTES (32 MiB)";
         default: return "unknown moe_route error code";
     }
 }

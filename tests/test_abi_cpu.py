@@ -31,7 +31,7 @@ def declared_functions():
 def test_every_declared_symbol_is_exported(lbs):
     lib = lbs.load()
     names = declared_functions()
-    assert set(names) == {"moe_route", "moe_route_backward", "moe_route_bias_update",
+    assert set(names) == {"moe_route", "moe_route_noalloc", "moe_route_backward", "moe_route_bias_update",
                           "moe_route_capacity", "moe_route_strerror", "moe_route_workspace_size",
                           "moe_gate_backward", "moe_gate_backward_workspace_size", "moe_eplb_plan",
                           "moe_sinkhorn_plan"}
@@ -207,6 +207,27 @@ def test_moe_route_validates_before_launching(lbs):
     assert bwd(ctypes.byref(pm), fake, None, fake, None, None, None, fake, None) == B.MOE_ERR_INVALID_ARG
     assert bwd(ctypes.byref(p), fake, None, fake, None, None, fake, fake, None) == B.MOE_ERR_INVALID_ARG
     assert bwd(ctypes.byref(p), fake, None, fake, None, fake + 2, fake, fake, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_noalloc_validates_before_any_device_work(lbs):
+    """moe_route_noalloc refuses a shape whose workspace exceeds the static
+    scratch (4096 microbatches of E=1024 need ~96 MiB) with MOE_ERR_SCRATCH,
+    and bad shapes with their usual codes, before touching the device (there
+    is no GPU here)."""
+    lib = lbs.load()
+    B = lbs._binding
+    fake = 0x10000
+    o = B.moe_route_out(*[fake for _ in B._OUT_FIELDS])
+    big = lbs.make_params(1 << 18, 1024, 32, n_micro=4096)
+    assert lbs.moe_route_workspace_size(big) > lbs.MOE_ROUTE_SCRATCH_BYTES
+    assert lib.moe_route_noalloc(ctypes.byref(big), fake, None, None, None, ctypes.byref(o),
+                                 None) == B.MOE_ERR_SCRATCH
+    assert "MOE_ROUTE_SCRATCH_BYTES" in lbs.moe_route_strerror(B.MOE_ERR_SCRATCH)
+    bad = lbs.make_params(16, 8, 9)
+    assert lib.moe_route_noalloc(ctypes.byref(bad), fake, None, None, None, ctypes.byref(o),
+                                 None) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_noalloc(None, fake, None, None, None, ctypes.byref(o),
+                                 None) == B.MOE_ERR_INVALID_ARG
 
 
 def test_gate_backward_validation(lbs):
