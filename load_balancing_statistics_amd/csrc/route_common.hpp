@@ -35,6 +35,20 @@ constexpr int kScanWaves = 16;     // waves per block-scan block
 constexpr int kScanPerWave = 8;    // row blocks per block-scan wave
 constexpr int kAssumedCUs = 256;   // MI355X compute units (grid sizing only)
 
+// Waves per row-pass block for S lanes per row and G columns per lane.  As
+// many waves per compute unit as the row pass's registers allow: 16 (4 per
+// SIMD) when a lane owns up to 16 columns, as two blocks of 8 (blocks of
+// half the rows: the combine and the scatter that follow work per row
+// block, and the scatter's smaller blocks overlap two per compute unit;
+// measured 1.5 us less a step at E=256 top-8 than one block of 16), 12 in
+// one block when a lane owns 24.  The selection-bias variant keeps G more
+// registers per lane: 12 waves when a lane owns up to 16 columns, 8 when it
+// owns 24.  One or two lanes per row with 16 columns hold more per-row state
+// per lane (ranking passes): 12 waves there too, so nothing spills.
+constexpr int rows_waves(int S, int G, bool bias) {
+    return bias ? ((G > 16) ? 8 : 12) : ((G > 16 || (S <= 2 && G >= 16)) ? 12 : 8);
+}
+
 inline int next_pow2(int v) {
     int p = 1;
     while (p < v) p <<= 1;
@@ -63,17 +77,7 @@ inline RowCfg choose_rows(int T, int E, int k, int n_micro, bool bias = false) {
     }
     // unaligned rows take the generic (bounds-checked) column path
     c.PAD = (S * c.G != E || c.VEC == 1) ? 1 : 0;
-    // As many waves per compute unit as the row pass's registers allow: 16
-    // (4 per SIMD) when a lane owns up to 16 columns, as two blocks of 8
-    // (blocks of half the rows: the combine and the scatter that follow
-    // work per row block, and the scatter's smaller blocks overlap two per
-    // compute unit; measured 1.5 us less a step at E=256 top-8 than one
-    // block of 16), 12 in one block when a lane owns 24.
-    // The selection-bias variant keeps G more registers per lane: 12 waves
-    // when a lane owns up to 16 columns, 8 when it owns 24.
-    // One or two lanes per row with 16 columns hold more per-row state per
-    // lane (ranking passes): 12 waves there too, so nothing spills.
-    c.NW = bias ? ((c.G > 16) ? 8 : 12) : ((c.G > 16 || (S <= 2 && c.G >= 16)) ? 12 : 8);
+    c.NW = rows_waves(S, c.G, bias);
     const int W = 64 / S;
     const long per_iter = long(c.NW) * W;
     const long Tm = T / n_micro;

@@ -151,7 +151,7 @@ __device__ __forceinline__ bool picked_col(float y, int col, float kv, int kc) {
     return y > kv || (y == kv && col <= kc);
 }
 
-template <int S, int G, int VEC, bool PAD, int NW, bool BIAS>
+template <int S, int G, int VEC, bool PAD, int NW, bool BIAS, bool MASKED>
 struct RowPass {
     static constexpr int W = 64 / S;               // rows per wave at a time
     static constexpr int RS = row_stride(S, G);    // LDS row-copy stride (floats)
@@ -279,7 +279,7 @@ struct RowPass {
         ssum = seg_sum<S>(ssum);
         const float inv = __builtin_amdgcn_rcpf(ssum);
         if (valid) {
-            if (!a.p_masked) {
+            if constexpr (!MASKED) {
 #pragma unroll
                 for (int g = 0; g < G; ++g) acc[g] = fmaf(ex[g], inv, acc[g]);
             }
@@ -342,28 +342,7 @@ struct RowPass {
                         wcol[p] = key_col(my);
                         const float lv = BIAS ? rowbuf[wcol[p]] : key_val(my);
                         we[p] = __builtin_amdgcn_exp2f(fmaf(lv, kLog2e, -mL));
-                        if (rank == k - 1) sel[0] = my;  // the k-th key, for masked P
-                    }
-                }
-            }
-            if (a.p_masked) {
-                // masked P: each owner adds the probabilities of its picked
-                // columns (recomputed here, so the all-token path keeps ex[]
-                // short-lived)
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-                const uint64_t kth = sel[0];
-                const float kv = key_val(kth);
-                const int kc = key_col(kth);
-                if (valid) {
-#pragma unroll
-                    for (int g = 0; g < G; ++g) {
-                        const int col = col_of<S, VEC>(g, s);
-                        const float y = BIAS ? x[g] + bz[g] : x[g];
-                        const float pv = __builtin_amdgcn_exp2f(fmaf(x[g], kLog2e, -mL));
-                        const bool pk = (!PAD || col < E) && picked_col(y, col, kv, kc);
-                        acc[g] = pk ? fmaf(pv, inv, acc[g]) : acc[g];
+                        if (MASKED && rank == k - 1) sel[0] = my;  // the k-th key, for masked P
                     }
                 }
             }
@@ -387,6 +366,32 @@ struct RowPass {
                 a.row_stats[2 * row] = m;
                 a.row_stats[2 * row + 1] = ssum;
             }
+        }
+
+        if constexpr (MASKED) {
+          if (!need_fb) {
+            // masked P: each owner adds the probabilities of its picked
+            // columns, recomputed from the LDS row copy (x[] and ex[]
+            // stay short-lived, so the all-token path keeps its
+            // registers)
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const uint64_t kth = sel[0];
+            const float kv = key_val(kth);
+            const int kc = key_col(kth);
+            if (valid) {
+#pragma unroll
+                for (int g = 0; g < G; ++g) {
+                    const int col = col_of<S, VEC>(g, s);
+                    const float xv = rowbuf[(!PAD || col < E) ? col : 0];
+                    const float y = BIAS ? xv + bz[g] : xv;
+                    const float pv = __builtin_amdgcn_exp2f(fmaf(xv, kLog2e, -mL));
+                    const bool pk = (!PAD || col < E) && picked_col(y, col, kv, kc);
+                    acc[g] = pk ? fmaf(pv, inv, acc[g]) : acc[g];
+                }
+            }
+          }
         }
     }
 
@@ -416,7 +421,7 @@ struct RowPass {
 #pragma unroll
             for (int g = 0; g < G; ++g) rowbuf[col_of<S, VEC>(g, s)] = x[g];
             const uint64_t kth = fallback_select(rowbuf, blds, sel, E, k, s);
-            if (a.p_masked && has) {
+            if (MASKED && has) {
                 const float kv = key_val(kth), inv = __builtin_amdgcn_rcpf(ssum);
                 const int kc = key_col(kth);
 #pragma unroll
@@ -452,12 +457,14 @@ struct RowPass {
 template <int NW, bool BIAS>
 constexpr int rows_min_waves_per_simd() { return (NW == 8 && !BIAS) ? 4 : 1; }
 
-template <int S, int G, int VEC, bool PAD, int NW, bool BIAS>
+// MASKED: P from each token's picks only (flag MOE_P_MASKED), a compile-time
+// variant so that the all-token kernels keep their register budget.
+template <int S, int G, int VEC, bool PAD, int NW, bool BIAS, bool MASKED>
 __global__ void __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(rows_min_waves_per_simd<NW, BIAS>())))
 route_rows_kernel(const RowsArgs a)
 {
-    using RP = RowPass<S, G, VEC, PAD, NW, BIAS>;
+    using RP = RowPass<S, G, VEC, PAD, NW, BIAS, MASKED>;
     constexpr int W = RP::W, RS = RP::RS, CS = RP::CS;
 
     extern __shared__ __align__(16) unsigned char smem[];
@@ -741,10 +748,12 @@ route_backward_kernel(const BackArgs a)
     }
 }
 
-template <int S, int G, int VEC, bool PAD, int NW, bool BIAS>
-hipError_t launch_rows_nw(const RowCfg& c, const RowsArgs& a, hipStream_t st) {
+template <int S, int G, int VEC, bool PAD, bool BIAS, bool MASKED>
+hipError_t launch_rows_v(const RowCfg& c, const RowsArgs& a, hipStream_t st) {
+    constexpr int NW = rows_waves(S, G, BIAS);
+    if (c.NW != NW) return hipErrorInvalidValue;
     const size_t lds = rows_lds_bytes(c, a.E, a.k, BIAS);
-    auto kern = route_rows_kernel<S, G, VEC, PAD, NW, BIAS>;
+    auto kern = route_rows_kernel<S, G, VEC, PAD, NW, BIAS, MASKED>;
     if (lds > 64 * 1024) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
@@ -756,14 +765,11 @@ hipError_t launch_rows_nw(const RowCfg& c, const RowsArgs& a, hipStream_t st) {
 
 template <int S, int G, int VEC, bool PAD>
 hipError_t launch_rows(const RowCfg& c, const RowsArgs& a, hipStream_t st) {
-    if (a.bias) {
-        if (c.NW == 12) return launch_rows_nw<S, G, VEC, PAD, 12, true>(c, a, st);
-        if (c.NW == 8) return launch_rows_nw<S, G, VEC, PAD, 8, true>(c, a, st);
-        return hipErrorInvalidValue;
-    }
-    if (c.NW == 8) return launch_rows_nw<S, G, VEC, PAD, 8, false>(c, a, st);
-    if (c.NW == 12) return launch_rows_nw<S, G, VEC, PAD, 12, false>(c, a, st);
-    return hipErrorInvalidValue;
+    if (a.bias)
+        return a.p_masked ? launch_rows_v<S, G, VEC, PAD, true, true>(c, a, st)
+                          : launch_rows_v<S, G, VEC, PAD, true, false>(c, a, st);
+    return a.p_masked ? launch_rows_v<S, G, VEC, PAD, false, true>(c, a, st)
+                      : launch_rows_v<S, G, VEC, PAD, false, false>(c, a, st);
 }
 
 template <int S, int G, int VEC, bool PAD, int NW, bool SP>
@@ -781,12 +787,12 @@ hipError_t launch_backward_nw(const RowCfg& c, const BackArgs& a, hipStream_t st
 
 template <int S, int G, int VEC, bool PAD>
 hipError_t launch_backward(const RowCfg& c, const BackArgs& a, hipStream_t st) {
+    // the backward's blocks are the forward's row blocks (no selection bias)
+    constexpr int NW = rows_waves(S, G, false);
+    if (c.NW != NW) return hipErrorInvalidValue;
     const bool sp = a.p_masked || a.d_topk_w;
-    if (c.NW == 8)
-        return sp ? launch_backward_nw<S, G, VEC, PAD, 8, true>(c, a, st)
-                  : launch_backward_nw<S, G, VEC, PAD, 8, false>(c, a, st);
-    return sp ? launch_backward_nw<S, G, VEC, PAD, 12, true>(c, a, st)
-              : launch_backward_nw<S, G, VEC, PAD, 12, false>(c, a, st);
+    return sp ? launch_backward_nw<S, G, VEC, PAD, NW, true>(c, a, st)
+              : launch_backward_nw<S, G, VEC, PAD, NW, false>(c, a, st);
 }
 
 // Dispatch over (G, VEC, PAD) for one S.
