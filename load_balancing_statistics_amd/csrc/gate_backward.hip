@@ -5,15 +5,17 @@
 // dlogits is the routing gradient with respect to the logits.
 //
 // Both products stream X (or dX) once and are bound by HBM (about 6 flop per
-// byte), fused in one pass.  For E <= 16 the reduction over tokens, dWg, runs
-// on the matrix cores (v_mfma_f32_16x16x4_f32, fp32 in and out): 16 lanes
-// share a row, lane n of a row holds CPL consecutive columns, and a step of
-// four rows is, for each of the lane's CPL column offsets q, the product of
-// A = dlogits [16 experts x 4 rows] (lane l: row l/16, expert l%16) and
-// B_q = X [4 rows x 16 columns] (lane l: row l/16, column CPL*(l%16) + q),
-// accumulated in a 16 x 16 tile per q.  dX stays on the vector ALUs: each
-// lane takes its row's E gradients from lanes 16*(l/16) + e (DPP row
-// broadcast) and forms its CPL outputs, rounded to bf16 in hardware.
+// byte), fused in one pass.  For E <= 16 both run on the matrix cores
+// (v_mfma_f32_16x16x4_f32, fp32 in and out).  dWg, the reduction over
+// tokens: 16 lanes share a row, lane n of a row holds CPL consecutive
+// columns, and a step of four rows is, for each of the lane's CPL column
+// offsets q, the product of A = dlogits [16 experts x 4 rows] (lane l: row
+// l/16, expert l%16) and B_q = X [4 rows x 16 columns] (lane l: row l/16,
+// column CPL*(l%16) + q), accumulated in a 16 x 16 tile per q.  dX, per 16
+// rows of a wave: see the kernel; its tile goes through LDS so that every
+// store writes whole runs of a row.  dX is stored nontemporally: nothing
+// here reads it again, and its dirty lines, written back later, would
+// otherwise slow the next kernel's reads of X by a third.
 //
 // For 16 < E <= 64 both products run on the vector ALUs.  A block owns a
 // 64-column tile of X over a contiguous slice of the tokens; a lane owns CPL
@@ -170,18 +172,45 @@ gate_backward_kernel(const GateBackArgs a)
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kMfWaves = 4;
 constexpr int kMfRowSteps = 8;  // 4-row steps whose loads are issued together
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// two fp32 -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
+}
 
 template <int CTRL>
 __device__ __forceinline__ float row_bcast(float v) {  // lane CTRL - 0x150 of the 16-lane row
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // EM: experts padded (8 or 16); CPL: columns per lane (tile = 16 * CPL).
+//
+// dWg: as described at the top.  dX on the matrix cores too: for each group
+// of 16 rows of the wave (four 4-row steps) and each 16-column tile t of the
+// block, D_t[i][j] = sum_e Wg[col(t,i)][e] * dlogits[row(j)][e] in EM/4
+// products of K = 4 (v_mfma_f32_16x16x4_f32: lane l gives A = Wg[col(t,l%16)]
+// [4h + l/16] and B = dlogits[row(l%16)][4h + l/16] and receives D[4(l/16)+m]
+// [l%16]).  With col(t, i) = 4*CPL*(i/4) + 4t + i%4, lane l ends up with
+// 4*CPL consecutive columns of row l%16; the tile is packed to bf16 and
+// passed through LDS, so that each store writes a row's columns of the X
+// layout (16 lanes per row, contiguous).
 template <int EM, int CPL>
 __global__ void __launch_bounds__(kMfWaves * 64)
 gate_backward_mfma_kernel(const GateBackArgs a)
 {
     constexpr int kTileM = 16 * CPL;
+    constexpr int KH = EM / 4;
+    constexpr int kPitch = kTileM * 2 + 16;   // bytes per staged dX row
+    __shared__ __attribute__((aligned(16))) unsigned char dxs[kMfWaves][16 * kPitch];
     const int E = a.E, d = a.d;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, r = lane >> 4;  // column group, row of the 4-row step
@@ -189,13 +218,18 @@ gate_backward_mfma_kernel(const GateBackArgs a)
     const bool col_ok = col0 < d;            // d % 8 == 0: a lane's columns are all in or all out
     const long t0 = (long(blockIdx.y) * a.T) / gridDim.y;
     const long t1 = (long(blockIdx.y + 1) * a.T) / gridDim.y;
+    unsigned char* stage = dxs[wave];
 
-    float wg[CPL][EM];
+    // dX A operands: Wg[col(t, n)][4h + r]
+    float wa[CPL][KH];
 #pragma unroll
-    for (int c = 0; c < CPL; ++c)
+    for (int t = 0; t < CPL; ++t)
 #pragma unroll
-        for (int e = 0; e < EM; ++e)
-            wg[c][e] = (col_ok && e < E) ? bf16_to_f32(a.Wg[long(col0 + c) * E + e]) : 0.f;
+        for (int h = 0; h < KH; ++h) {
+            const int c = blockIdx.x * kTileM + 4 * CPL * (n >> 2) + 4 * t + (n & 3);
+            const int e = 4 * h + r;
+            wa[t][h] = (a.dX && c < d && e < E) ? bf16_to_f32(a.Wg[long(c) * E + e]) : 0.f;
+        }
     f32x4 acc[CPL];
 #pragma unroll
     for (int q = 0; q < CPL; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -204,6 +238,7 @@ gate_backward_mfma_kernel(const GateBackArgs a)
     for (long s0 = t0 + 4L * wave; s0 < t1; s0 += step * kMfRowSteps) {
         uint32_t xv[kMfRowSteps][CPL / 2];
         float dv[kMfRowSteps];
+        float gb[kMfRowSteps / 4][KH];
 #pragma unroll
         for (int u = 0; u < kMfRowSteps; ++u) {
             const long row = s0 + u * step + r;
@@ -219,9 +254,20 @@ gate_backward_mfma_kernel(const GateBackArgs a)
             const float g = (n < E) ? a.dlogits[rr * E + n] : 0.f;
             dv[u] = in ? g : 0.f;  // rows past the slice add nothing to dWg
         }
+        if (a.dX) {
+            // B operands of the two 16-row groups: row(G, j) = s0 + (4G + j/4)*step + j%4, j = n
+#pragma unroll
+            for (int G = 0; G < kMfRowSteps / 4; ++G) {
+                const long row = s0 + (4 * G + (n >> 2)) * step + (n & 3);
+#pragma unroll
+                for (int h = 0; h < KH; ++h) {
+                    const int e = 4 * h + r;
+                    gb[G][h] = (row < t1 && e < E) ? a.dlogits[row * E + e] : 0.f;
+                }
+            }
+        }
 #pragma unroll
         for (int u = 0; u < kMfRowSteps; ++u) {
-            const long row = s0 + u * step + r;
             float x[CPL];
 #pragma unroll
             for (int h = 0; h < CPL / 2; ++h) {
@@ -230,38 +276,48 @@ gate_backward_mfma_kernel(const GateBackArgs a)
             }
 #pragma unroll
             for (int q = 0; q < CPL; ++q) acc[q] = __builtin_amdgcn_mfma_f32_16x16x4f32(dv[u], x[q], acc[q], 0, 0, 0);
-            if (a.dX) {
-                // the broadcasts read lanes 16*(l/16) + e, which must be active:
-                // taken by the whole wave, before the per-lane bounds
-                float g[EM];
-                g[0] = row_bcast<0x150>(dv[u]); g[1] = row_bcast<0x151>(dv[u]);
-                g[2] = row_bcast<0x152>(dv[u]); g[3] = row_bcast<0x153>(dv[u]);
-                g[4] = row_bcast<0x154>(dv[u]); g[5] = row_bcast<0x155>(dv[u]);
-                g[6] = row_bcast<0x156>(dv[u]); g[7] = row_bcast<0x157>(dv[u]);
-                if constexpr (EM == 16) {
-                    g[8 % EM] = row_bcast<0x158>(dv[u]); g[9 % EM] = row_bcast<0x159>(dv[u]);
-                    g[10 % EM] = row_bcast<0x15A>(dv[u]); g[11 % EM] = row_bcast<0x15B>(dv[u]);
-                    g[12 % EM] = row_bcast<0x15C>(dv[u]); g[13 % EM] = row_bcast<0x15D>(dv[u]);
-                    g[14 % EM] = row_bcast<0x15E>(dv[u]); g[15 % EM] = row_bcast<0x15F>(dv[u]);
+        }
+        if (a.dX) {
+#pragma unroll
+            for (int G = 0; G < kMfRowSteps / 4; ++G) {
+                // all tiles' products first (independent accumulators), then the packing
+                f32x4 o[CPL];
+#pragma unroll
+                for (int t = 0; t < CPL; ++t)
+                    o[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[t][0], gb[G][0], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+                for (int h = 1; h < KH; ++h)
+#pragma unroll
+                    for (int t = 0; t < CPL; ++t) o[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(wa[t][h], gb[G][h], o[t], 0, 0, 0);
+                uint32_t pk[2 * CPL];
+#pragma unroll
+                for (int t = 0; t < CPL; ++t) {
+                    pk[2 * t] = pack_bf16x2(o[t][0], o[t][1]);
+                    pk[2 * t + 1] = pack_bf16x2(o[t][2], o[t][3]);
                 }
-                if (col_ok && row < t1) {
-                    uint32_t pk[CPL / 2];
+                // row n of the tile, columns 4*CPL*r .. +4*CPL
 #pragma unroll
-                    for (int h = 0; h < CPL / 2; ++h) {
-                        float o0 = 0.f, o1 = 0.f;
+                for (int w = 0; w < CPL / 2; ++w)
+                    *reinterpret_cast<uint4*>(stage + n * kPitch + 8 * CPL * r + 16 * w) =
+                        make_uint4(pk[4 * w], pk[4 * w + 1], pk[4 * w + 2], pk[4 * w + 3]);
+                wave_lds_sync();
 #pragma unroll
-                        for (int e = 0; e < EM; ++e) {
-                            o0 = fmaf(g[e], wg[2 * h][e], o0);
-                            o1 = fmaf(g[e], wg[2 * h + 1][e], o1);
+                for (int sidx = 0; sidx < 4; ++sidx) {
+                    const long row = s0 + (4 * G + sidx) * step + r;
+                    const unsigned char* src = stage + (4 * sidx + r) * kPitch + 2 * CPL * n;
+                    if (col_ok && row < t1) {
+                        // nontemporal: dX is not read again here, and written-back
+                        // lines would otherwise stall the next kernel's reads
+                        if constexpr (CPL == 8) {
+                            const u32x4 v = *reinterpret_cast<const u32x4*>(src);
+                            __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(a.dX + row * d + col0));
+                        } else {
+                            const u32x2 v = *reinterpret_cast<const u32x2*>(src);
+                            __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(a.dX + row * d + col0));
                         }
-                        pk[h] = uint32_t(__builtin_bit_cast(uint16_t, (__bf16)o0)) |
-                                (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)o1)) << 16);
                     }
-                    if constexpr (CPL == 8)
-                        *reinterpret_cast<uint4*>(a.dX + row * d + col0) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-                    else
-                        *reinterpret_cast<uint2*>(a.dX + row * d + col0) = make_uint2(pk[0], pk[1]);
                 }
+                wave_lds_sync();
             }
         }
     }
@@ -290,13 +346,22 @@ gate_backward_mfma_kernel(const GateBackArgs a)
     }
 }
 
-// dWg[i] = sum over the token slices of part[slice][i], slices in order.
+// dWg[i] = sum over the token slices of part[slice][i], slices in order
+// (eight loads in flight at a time, the additions still in slice order).
 __global__ void __launch_bounds__(256)
 gate_backward_reduce_kernel(const float* __restrict__ part, float* __restrict__ dWg, long n, int slices)
 {
     for (long i = long(blockIdx.x) * 256 + threadIdx.x; i < n; i += long(gridDim.x) * 256) {
         float s = 0.f;
-        for (int sl = 0; sl < slices; ++sl) s += part[long(sl) * n + i];
+        int sl = 0;
+        for (; sl + 8 <= slices; sl += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = part[long(sl + u) * n + i];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) s += v[u];
+        }
+        for (; sl < slices; ++sl) s += part[long(sl) * n + i];
         dWg[i] = s;
     }
 }

@@ -7,16 +7,22 @@
 // by the matrix cores.
 //
 // MFMA v_mfma_f32_16x16x32_bf16: A = 16 tokens x 32 k, B = 32 k x 16 experts.
-// Lane l holds A[l%16][8*(l/16) .. +8) (16 contiguous bytes of one X row) and
-// B[8*(l/16) .. +8)[l%16]; the result D[i][j] sits in lane j + 16*(i/4),
-// element i%4.  B wants 8 consecutive k of one expert, which Wg [d,E]
-// (expert-minor) does not store contiguously, so a first tiny kernel writes
-// Wg transposed, Wt [E,d], into the workspace; the GEMM then reads 16 bytes
-// per lane for A (HBM) and for B (L2-resident Wt).
+// Lane l holds A[l%16][8*(l/16) .. +8) and B[8*(l/16) .. +8)[l%16]; the
+// result D[i][j] sits in lane j + 16*(i/4), element i%4.
 //
-// A block computes a 16-token tile; its 4 waves split the k range into four
-// contiguous quarters and the partial tiles are summed in a fixed order in
-// LDS (deterministic).
+// Operand A is 16 bytes of one X row per lane, 16 different rows across
+// consecutive lanes: loaded like that, every quad of lanes touches four cache
+// lines and the address unit, not HBM, limits the kernel.  So a wave loads
+// its tile of X coalesced (16 lanes cover 256 contiguous bytes of a row),
+// stores it in LDS (row pitch 272 bytes: the 16 rows an MFMA operand read
+// touches fall in distinct banks) and reads the operands back from there.
+// Operand B is laid out once per call by a tiny kernel, Wb[step][tile][lane]
+// (16 bytes each, zero past d and E), so its loads are contiguous per wave.
+//
+// A block computes 32 tokens (two 16-token tiles); its 4 waves split the k
+// range into four contiguous quarters, staging 128 k (256 bytes per row) at a
+// time, and the partial tiles are summed in a fixed order in LDS
+// (deterministic).
 #include "route_common.hpp"
 
 namespace moe {
@@ -26,86 +32,134 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGateWaves = 4;
-constexpr int kUnroll = 8;
-constexpr int kMaxTilesN = 4;  // E <= 64
+constexpr int kMaxTilesN = 4;              // E <= 64
+constexpr int kMT = 2;                     // 16-token tiles per block
+constexpr int kRows = 16 * kMT;            // tokens per block
+constexpr int kChunkK = 128;               // k staged at a time
+constexpr int kSteps = kChunkK / 32;       // MFMA steps per chunk
+constexpr int kRowPitch = kChunkK * 2 + 16;
+constexpr int kLanesPerRow = kChunkK / 8;  // 16 bytes per lane
+constexpr int kRowsPerLoad = 64 / kLanesPerRow;
+constexpr int kLoads = kRows / kRowsPerLoad;
 
+// Wb[(s*NT + t)*64 + l] = bf16 Wg[32s + 8(l/16) + j][16t + l%16], j = 0..7
 __global__ void __launch_bounds__(256)
-transpose_wg_kernel(const uint16_t* __restrict__ Wg, uint16_t* __restrict__ Wt, int d, int E)
+swizzle_wg_kernel(const uint16_t* __restrict__ Wg, uint4* __restrict__ Wb, int d, int E, int NT, long n)
 {
-    const long n = long(d) * E;
-    for (long i = long(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-         i += long(gridDim.x) * blockDim.x) {
-        const long kk = i / E, e = i % E;  // Wg[kk][e]
-        Wt[e * d + kk] = Wg[i];
+    for (long i = long(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += long(gridDim.x) * blockDim.x) {
+        const int l = int(i % 64);
+        const long st = i / 64;
+        const int t = int(st % NT);
+        const long s = st / NT;
+        const int e = t * 16 + (l & 15);
+        const long k0 = 32 * s + 8 * (l >> 4);
+        uint32_t w[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+            const long ka = k0 + 2 * h, kb = ka + 1;
+            const uint32_t lo = (e < E && ka < d) ? Wg[ka * E + e] : 0u;
+            const uint32_t hi = (e < E && kb < d) ? Wg[kb * E + e] : 0u;
+            w[h] = lo | (hi << 16);
+        }
+        Wb[i] = make_uint4(w[0], w[1], w[2], w[3]);
     }
 }
 
-__device__ __forceinline__ bf16x8 load8(const uint16_t* p) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    return __builtin_bit_cast(bf16x8, v);
-}
-
-__device__ __forceinline__ bf16x8 zero8() {
-    return __builtin_bit_cast(bf16x8, make_uint4(0, 0, 0, 0));
+// LDS writes by some lanes, then reads of them by others, within one wave
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 template <int NT>
 __global__ void __launch_bounds__(kGateWaves * 64)
-gate_gemm_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wt,
+gate_gemm_kernel(const uint16_t* __restrict__ X, const uint4* __restrict__ Wb,
                  float* __restrict__ logits, int T, int d, int E)
 {
-    __shared__ f32x4 red[kGateWaves][NT][64];
+    constexpr int kStage = kRows * kRowPitch;
+    constexpr int kRed = kGateWaves * kMT * NT * 64 * 16;
+    constexpr int kLds = kGateWaves * kStage > kRed ? kGateWaves * kStage : kRed;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, kq = lane >> 4;
-    const long row = long(blockIdx.x) * 16 + r16;
-    const bool row_ok = row < T;
-    const int nsteps = (d + 31) / 32;
-    const int per = (nsteps + kGateWaves - 1) / kGateWaves;
-    const int st0 = min(wave * per, nsteps), st1 = min(st0 + per, nsteps);
+    const long row0 = long(blockIdx.x) * kRows;
+    const int nchunks = (d + kChunkK - 1) / kChunkK;
+    const int per = (nchunks + kGateWaves - 1) / kGateWaves;
+    const int c0 = min(wave * per, nchunks), c1 = min(c0 + per, nchunks);
+    unsigned char* stage = lds + wave * kStage;
 
-    f32x4 acc[NT];
+    f32x4 acc[kMT][NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < kMT; ++m)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const uint16_t* xrow = X + row * d;
-    for (int s0 = st0; s0 < st1; s0 += kUnroll) {
-        bf16x8 av[kUnroll];
-        bf16x8 bv[kUnroll][NT];
+    // coalesced loads: load j covers rows kRowsPerLoad*j + lr, lane's 8 k at lc
+    const int lr = lane / kLanesPerRow, lc = (lane % kLanesPerRow) * 8;
+    uint4 xr[kLoads];
+    auto load_chunk = [&](int c) {
+        const int k = c * kChunkK + lc;  // d % 8 == 0: the lane's 8 k are all in or all out
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int kk = (s0 + u) * 32 + kq * 8;
-            const bool kin = (s0 + u < st1) && (kk < d);
-            av[u] = (row_ok && kin) ? load8(xrow + kk) : zero8();
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const int e = t * 16 + r16;
-                bv[u][t] = (kin && e < E) ? load8(Wt + long(e) * d + kk) : zero8();
-            }
+        for (int j = 0; j < kLoads; ++j) {
+            const long row = row0 + kRowsPerLoad * j + lr;
+            xr[j] = (row < T && k < d) ? *reinterpret_cast<const uint4*>(X + row * d + k)
+                                       : make_uint4(0, 0, 0, 0);
         }
+    };
+    if (c0 < c1) load_chunk(c0);
+    for (int c = c0; c < c1; ++c) {
+        uint4 bv[kSteps][NT];
 #pragma unroll
-        for (int u = 0; u < kUnroll; ++u)
+        for (int s = 0; s < kSteps; ++s)
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bv[u][t], acc[t], 0, 0, 0);
+            for (int t = 0; t < NT; ++t) bv[s][t] = Wb[(long(c * kSteps + s) * NT + t) * 64 + lane];
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j)
+            *reinterpret_cast<uint4*>(stage + (kRowsPerLoad * j + lr) * kRowPitch + (lane % kLanesPerRow) * 16) = xr[j];
+        wave_lds_sync();
+        if (c + 1 < c1) load_chunk(c + 1);  // in flight while this chunk is multiplied
+#pragma unroll
+        for (int s = 0; s < kSteps; ++s)
+#pragma unroll
+            for (int m = 0; m < kMT; ++m) {
+                const uint4 av = *reinterpret_cast<const uint4*>(stage + (m * 16 + r16) * kRowPitch + s * 64 + kq * 16);
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    acc[m][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, av),
+                                                                       __builtin_bit_cast(bf16x8, bv[s][t]),
+                                                                       acc[m][t], 0, 0, 0);
+            }
+        wave_lds_sync();  // the next chunk overwrites the stage
     }
 
-#pragma unroll
-    for (int t = 0; t < NT; ++t) red[wave][t][lane] = acc[t];
     __syncthreads();
-    if (wave == 0) {
+    f32x4* red = reinterpret_cast<f32x4*>(lds);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            f32x4 sum = red[0][t][lane];
+    for (int m = 0; m < kMT; ++m)
 #pragma unroll
-            for (int w = 1; w < kGateWaves; ++w) sum += red[w][t][lane];
-            const int col = t * 16 + r16;
+        for (int t = 0; t < NT; ++t) red[((wave * kMT + m) * NT + t) * 64 + lane] = acc[m][t];
+    __syncthreads();
+    for (int q = wave; q < kMT * NT; q += kGateWaves) {
+        const int m = q / NT, t = q % NT;
+        f32x4 sum = red[(m * NT + t) * 64 + lane];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const long r = long(blockIdx.x) * 16 + kq * 4 + i;
-                if (r < T && col < E) logits[r * E + col] = sum[i];
-            }
+        for (int w = 1; w < kGateWaves; ++w) sum += red[((w * kMT + m) * NT + t) * 64 + lane];
+        const int col = t * 16 + r16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const long r = row0 + m * 16 + kq * 4 + i;
+            if (r < T && col < E) logits[r * E + col] = sum[i];
         }
     }
+}
+
+int gate_tiles_n(int E) { return (E + 15) / 16; }
+
+// 16-byte units of the laid-out B operand: every MFMA step of every chunk
+long gate_wb_units(int d, int E) {
+    const long nchunks = (d + kChunkK - 1) / kChunkK;
+    return nchunks * kSteps * gate_tiles_n(E) * 64;
 }
 
 }  // namespace
@@ -114,21 +168,22 @@ bool gate_supported(int T, int d, int E) {
     return T >= 1 && d >= 8 && d % 8 == 0 && E >= 1 && E <= 16 * kMaxTilesN;
 }
 
-size_t gate_workspace_bytes(int d, int E) { return align_up(size_t(d) * E * 2, 256); }
+size_t gate_workspace_bytes(int d, int E) { return align_up(size_t(gate_wb_units(d, E)) * 16, 256); }
 
 hipError_t launch_gate_gemm(const GateArgs& a, uint16_t* wt, hipStream_t st) {
-    const long n = long(a.d) * a.E;
+    const int nt = gate_tiles_n(a.E);
+    const long n = gate_wb_units(a.d, a.E);
+    uint4* wb = reinterpret_cast<uint4*>(wt);
     const int tb = int(std::min<long>((n + 255) / 256, 1024));
-    hipLaunchKernelGGL(transpose_wg_kernel, dim3(tb), dim3(256), 0, st, a.Wg, wt, a.d, a.E);
+    hipLaunchKernelGGL(swizzle_wg_kernel, dim3(tb), dim3(256), 0, st, a.Wg, wb, a.d, a.E, nt, n);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const dim3 grid((a.T + 15) / 16);
-    const int nt = (a.E + 15) / 16;
+    const dim3 grid((a.T + kRows - 1) / kRows);
     switch (nt) {
-        case 1: hipLaunchKernelGGL(gate_gemm_kernel<1>, grid, dim3(256), 0, st, a.X, wt, a.logits, a.T, a.d, a.E); break;
-        case 2: hipLaunchKernelGGL(gate_gemm_kernel<2>, grid, dim3(256), 0, st, a.X, wt, a.logits, a.T, a.d, a.E); break;
-        case 3: hipLaunchKernelGGL(gate_gemm_kernel<3>, grid, dim3(256), 0, st, a.X, wt, a.logits, a.T, a.d, a.E); break;
-        case 4: hipLaunchKernelGGL(gate_gemm_kernel<4>, grid, dim3(256), 0, st, a.X, wt, a.logits, a.T, a.d, a.E); break;
+        case 1: hipLaunchKernelGGL(gate_gemm_kernel<1>, grid, dim3(256), 0, st, a.X, wb, a.logits, a.T, a.d, a.E); break;
+        case 2: hipLaunchKernelGGL(gate_gemm_kernel<2>, grid, dim3(256), 0, st, a.X, wb, a.logits, a.T, a.d, a.E); break;
+        case 3: hipLaunchKernelGGL(gate_gemm_kernel<3>, grid, dim3(256), 0, st, a.X, wb, a.logits, a.T, a.d, a.E); break;
+        case 4: hipLaunchKernelGGL(gate_gemm_kernel<4>, grid, dim3(256), 0, st, a.X, wb, a.logits, a.T, a.d, a.E); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

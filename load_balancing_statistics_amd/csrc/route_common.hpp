@@ -150,7 +150,7 @@ struct Workspace {
     int32_t* colprefix;   // [B,E]        exclusive prefix over the blocks of a split
     int32_t* split_tot;   // [m,nsplit,E] counts per split
     double*  split_P;     // [m,nsplit,E] probability sums per split
-    uint16_t* Wt;         // [E,d]        transposed gate weights (gate path only)
+    uint16_t* Wt;         // gate weights laid out as the MFMA B operand (gate path only)
     size_t   bytes;
 };
 
