@@ -127,13 +127,19 @@ def measured_traffic(workload, kernel_prefix):
     return None
 
 
-def host_cores():
-    """Cores this process may run on, capped at the 16 a one-GPU machine shares."""
+def affinity_cores():
+    """Cores the scheduler lets this process run on."""
     try:
-        n = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(16, n))
+        return os.cpu_count() or 1
+
+
+def host_cores():
+    """Worker threads for the CPU leg: the affinity, capped at 16 -- the CPU
+    share of a one-GPU slot on an 8-GPU host, however many cores the
+    scheduler shows (a larger pool competes with the other slots' jobs)."""
+    return max(1, min(16, affinity_cores()))
 
 
 def cpu_baseline(w, inp, budget_s):
@@ -216,7 +222,8 @@ def cpu_baseline(w, inp, budget_s):
                else f"one thread, x{reps} pass(es) (faster than {len(bounds)} threads on chunks "
                     f"of ~{chunk} tokens)"))
     return {"value": legs[best]["value"], "unit": "tokens/s", "cores": legs[best]["cores"],
-            "kind": "oracle", "sample": sample, "seconds": legs[best]["seconds"], **legs}
+            "affinity_cores": affinity_cores(), "kind": "oracle", "sample": sample,
+            "seconds": legs[best]["seconds"], **legs}
 
 
 PLANNERS = ("eplb_v4", "sinkhorn_r64")
