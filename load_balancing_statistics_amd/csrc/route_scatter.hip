@@ -81,20 +81,17 @@ __device__ void microbatch_statistics(const ScatterArgs& a, int mb, const int* t
         if (a.P) a.P[cb + e] = float(pe);
         q[e] = fe * pe;
         q[E + e] = (double(cnt) - mean) * (double(cnt) - mean);
-        q[2 * E + e] = fe > 0.0 ? -fe * log(fe) : 0.0;
+        // -f ln f with a hardware fp32 log2 (about 1e-7 relative per term;
+        // the terms share one sign, so the sum keeps that precision)
+        q[2 * E + e] = fe > 0.0 ? -fe * (double(__builtin_amdgcn_logf(float(fe))) * 0.69314718055994531) : 0.0;
         q[3 * E + e] = double((a.capacity >= 0 && cnt > a.capacity) ? a.capacity : cnt);
     }
     __syncthreads();
-    constexpr int kStrides = (MOE_ROUTE_MAX_E + 63) / 64;
     if (wave < 4) {
         // sum of terms: f.P, squared deviations, entropy terms, kept
         const double* v = q + wave * E;
         double acc = 0.0;
-#pragma unroll
-        for (int i = 0; i < kStrides; ++i) {
-            const int e = lane + 64 * i;
-            acc += (e < E) ? v[e] : 0.0;
-        }
+        for (int e = lane; e < E; e += 64) acc += v[e];
         acc = wave_sum_f64(acc);
         if (lane == 0) {
             float* x = a.extra ? a.extra + long(mb) * 8 : nullptr;
@@ -114,11 +111,7 @@ __device__ void microbatch_statistics(const ScatterArgs& a, int mb, const int* t
     } else if (wave < 6) {
         // largest (wave 4) and smallest (wave 5) count
         int m = (wave == 4) ? -1 : INT_MAX;
-#pragma unroll
-        for (int i = 0; i < kStrides; ++i) {
-            const int e = lane + 64 * i;
-            if (e < E) m = (wave == 4) ? max(m, tot[e]) : min(m, tot[e]);
-        }
+        for (int e = lane; e < E; e += 64) m = (wave == 4) ? max(m, tot[e]) : min(m, tot[e]);
         m = (wave == 4) ? wave_max_i(m) : wave_min_i(m);
         if (lane == 0) {
             float* x = a.extra ? a.extra + long(mb) * 8 : nullptr;
@@ -317,36 +310,33 @@ route_scatter_kernel(const ScatterArgs a)
         // From the combine kernel: the split sums and this block's prefix
         // inside its split; the first kSplitBatch splits are loaded with the
         // prefix, in one round, and in the first block of the microbatch
-        // with the probability sums.
-        if (stats_block) {
+        // the probability sums with them (one round trip, not two).
 #pragma unroll
-            for (int it = 0; it < EPT; ++it) {
-                const int e = tid + it * NW * 64;
-                if (e >= E) break;
-                const long sb = long(mb) * a.nsplit * E + e;
-                for (int sp0 = 0; sp0 < a.nsplit; sp0 += kSplitBatch) {
-                    double pv[kSplitBatch];
-#pragma unroll
-                    for (int v = 0; v < kSplitBatch; ++v)
-                        pv[v] = load_or(a.split_P, sb + long(sp0 + v) * E, sp0 + v < a.nsplit, 0.0);
-#pragma unroll
-                    for (int v = 0; v < kSplitBatch; ++v) psum[it] += pv[v];
-                }
-            }
-        }
-        for (int e = tid; e < E; e += NW * 64) {
+        for (int it = 0; it < EPT; ++it) {
+            const int e = tid + it * NW * 64;
+            if (e >= E) break;
             const long sb = long(mb) * a.nsplit * E + e;
             const int cp = a.colprefix[long(b) * E + e];
             int t = 0, pre = 0;
             for (int sp0 = 0; sp0 < a.nsplit; sp0 += kSplitBatch) {
                 int sv[kSplitBatch];
+                double pv[kSplitBatch];
 #pragma unroll
                 for (int v = 0; v < kSplitBatch; ++v)
                     sv[v] = load_or(a.split_tot, sb + long(sp0 + v) * E, sp0 + v < a.nsplit, 0);
+                if (stats_block) {
+#pragma unroll
+                    for (int v = 0; v < kSplitBatch; ++v)
+                        pv[v] = load_or(a.split_P, sb + long(sp0 + v) * E, sp0 + v < a.nsplit, 0.0);
+                }
 #pragma unroll
                 for (int v = 0; v < kSplitBatch; ++v) {
                     t += sv[v];
                     pre += (sp0 + v < my_split) ? sv[v] : 0;
+                }
+                if (stats_block) {
+#pragma unroll
+                    for (int v = 0; v < kSplitBatch; ++v) psum[it] += pv[v];
                 }
             }
             tot[e] = t;
