@@ -115,9 +115,11 @@ typedef struct {
  *                          max f, min f ([p2] 4.2)
  *   status   [1] int32     nullable; MOE_STATUS_* bits of this call
  *   row_pass_events        nullable pair of hipEvent_t handles created by the
- *                          caller; when both are set the library records
- *                          them on the stream right before and right after
- *                          the row-pass kernel (per-kernel timing)
+ *                          caller; when both are set the row-pass kernel is
+ *                          launched with them as its start and stop events
+ *                          (hipExtLaunchKernel: the runtime stamps them from
+ *                          that kernel's own dispatch, as a kernel trace
+ *                          does; hipEventElapsedTime then gives its time)
  */
 typedef struct {
     int32_t *topk_idx;

@@ -153,7 +153,7 @@ def moe_route(params, out, workspace, logits=None, X=None, Wg=None, stream=None,
     MOE_SELECT_BIAS (expert choice on logits + bias, weights unbiased).
 
     ``row_pass_events``: optional pair of raw hipEvent_t handles (ints) that the
-    library records around the row-pass kernel."""
+    library attaches to the row-pass kernel's launch as its start and stop."""
     o = moe_route_out(*[None if out.get(n) is None else out[n].data_ptr() for n in _OUT_FIELDS])
     if row_pass_events is not None:
         o.row_pass_events[0] = row_pass_events[0]

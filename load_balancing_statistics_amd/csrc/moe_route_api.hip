@@ -96,15 +96,15 @@ int scratch_of_current_device(void** out) {
 
 namespace moe {
 
-hipError_t launch_route_rows(const RowCfg& c, const RowsArgs& a, hipStream_t st) {
+hipError_t launch_route_rows(const RowCfg& c, const RowsArgs& a, hipStream_t st, const LaunchEvents* ev) {
     switch (c.S) {
-        case 1: return launch_rows_s<1>(c, a, st);
-        case 2: return launch_rows_s<2>(c, a, st);
-        case 4: return launch_rows_s<4>(c, a, st);
-        case 8: return launch_rows_s<8>(c, a, st);
-        case 16: return launch_rows_s<16>(c, a, st);
-        case 32: return launch_rows_s<32>(c, a, st);
-        case 64: return launch_rows_s<64>(c, a, st);
+        case 1: return launch_rows_s<1>(c, a, st, ev);
+        case 2: return launch_rows_s<2>(c, a, st, ev);
+        case 4: return launch_rows_s<4>(c, a, st, ev);
+        case 8: return launch_rows_s<8>(c, a, st, ev);
+        case 16: return launch_rows_s<16>(c, a, st, ev);
+        case 32: return launch_rows_s<32>(c, a, st, ev);
+        case 64: return launch_rows_s<64>(c, a, st, ev);
         default: return hipErrorInvalidValue;
     }
 }
@@ -195,11 +195,9 @@ int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
     ra.cnt_part = ws.cnt_part; ra.P_part = ws.P_part; ra.flag_part = ws.flag_part;
     ra.status = out->status;
     const bool timed = out->row_pass_events[0] && out->row_pass_events[1];
-    if (timed && hipEventRecord(static_cast<hipEvent_t>(out->row_pass_events[0]), st) != hipSuccess)
-        return MOE_ERR_HIP;
-    if (moe::launch_route_rows(c, ra, st) != hipSuccess) return MOE_ERR_HIP;
-    if (timed && hipEventRecord(static_cast<hipEvent_t>(out->row_pass_events[1]), st) != hipSuccess)
-        return MOE_ERR_HIP;
+    const moe::LaunchEvents ev{static_cast<hipEvent_t>(out->row_pass_events[0]),
+                               static_cast<hipEvent_t>(out->row_pass_events[1])};
+    if (moe::launch_route_rows(c, ra, st, timed ? &ev : nullptr) != hipSuccess) return MOE_ERR_HIP;
 
     moe::ScanArgs sa{};
     sa.cnt_part = ws.cnt_part; sa.P_part = ws.P_part; sa.flag_part = ws.flag_part;

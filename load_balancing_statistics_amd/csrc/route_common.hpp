@@ -7,6 +7,7 @@
 // S consecutive floats of one row and a wave reads 64/S rows at once.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -311,14 +312,21 @@ struct GateArgs {
     int T, d, E;
 };
 
+// Optional timing of one launch: the runtime stamps start and stop from the
+// kernel's own dispatch (hipExtLaunchKernel), as a kernel trace does.
+struct LaunchEvents {
+    hipEvent_t start;
+    hipEvent_t stop;
+};
+
 // Launchers (each defined next to its kernel).  Return a hipError_t.
-hipError_t launch_route_rows(const RowCfg& c, const RowsArgs& a, hipStream_t st);
+hipError_t launch_route_rows(const RowCfg& c, const RowsArgs& a, hipStream_t st, const LaunchEvents* ev);
 template <int S>
-hipError_t launch_rows_s(const RowCfg& c, const RowsArgs& a, hipStream_t st);
+hipError_t launch_rows_s(const RowCfg& c, const RowsArgs& a, hipStream_t st, const LaunchEvents* ev);
 template <int S>
 hipError_t launch_backward_s(const RowCfg& c, const BackArgs& a, hipStream_t st);
 #define MOE_DECLARE_SEGMENT(SV)                                                           \
-    template <> hipError_t launch_rows_s<SV>(const RowCfg&, const RowsArgs&, hipStream_t); \
+    template <> hipError_t launch_rows_s<SV>(const RowCfg&, const RowsArgs&, hipStream_t, const LaunchEvents*); \
     template <> hipError_t launch_backward_s<SV>(const RowCfg&, const BackArgs&, hipStream_t);
 MOE_DECLARE_SEGMENT(1) MOE_DECLARE_SEGMENT(2) MOE_DECLARE_SEGMENT(4) MOE_DECLARE_SEGMENT(8)
 MOE_DECLARE_SEGMENT(16) MOE_DECLARE_SEGMENT(32) MOE_DECLARE_SEGMENT(64)

@@ -760,7 +760,7 @@ route_backward_kernel(const BackArgs a)
 }
 
 template <int S, int G, int VEC, bool PAD, bool BIAS, bool MASKED>
-hipError_t launch_rows_v(const RowCfg& c, const RowsArgs& a, hipStream_t st) {
+hipError_t launch_rows_v(const RowCfg& c, const RowsArgs& a, hipStream_t st, const LaunchEvents* ev) {
     constexpr int NW = rows_waves(S, G, BIAS);
     if (c.NW != NW) return hipErrorInvalidValue;
     const size_t lds = rows_lds_bytes(c, a.E, a.k, BIAS);
@@ -770,17 +770,20 @@ hipError_t launch_rows_v(const RowCfg& c, const RowsArgs& a, hipStream_t st) {
                                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(kern, dim3(c.B), dim3(NW * 64), lds, st, a);
+    if (ev && (ev->start || ev->stop))
+        hipExtLaunchKernelGGL(kern, dim3(c.B), dim3(NW * 64), lds, st, ev->start, ev->stop, 0u, a);
+    else
+        hipLaunchKernelGGL(kern, dim3(c.B), dim3(NW * 64), lds, st, a);
     return hipGetLastError();
 }
 
 template <int S, int G, int VEC, bool PAD>
-hipError_t launch_rows(const RowCfg& c, const RowsArgs& a, hipStream_t st) {
+hipError_t launch_rows(const RowCfg& c, const RowsArgs& a, hipStream_t st, const LaunchEvents* ev) {
     if (a.bias)
-        return a.p_masked ? launch_rows_v<S, G, VEC, PAD, true, true>(c, a, st)
-                          : launch_rows_v<S, G, VEC, PAD, true, false>(c, a, st);
-    return a.p_masked ? launch_rows_v<S, G, VEC, PAD, false, true>(c, a, st)
-                      : launch_rows_v<S, G, VEC, PAD, false, false>(c, a, st);
+        return a.p_masked ? launch_rows_v<S, G, VEC, PAD, true, true>(c, a, st, ev)
+                          : launch_rows_v<S, G, VEC, PAD, true, false>(c, a, st, ev);
+    return a.p_masked ? launch_rows_v<S, G, VEC, PAD, false, true>(c, a, st, ev)
+                      : launch_rows_v<S, G, VEC, PAD, false, false>(c, a, st, ev);
 }
 
 template <int S, int G, int VEC, bool PAD, int NW, bool SP>
@@ -797,7 +800,7 @@ hipError_t launch_backward_nw(const RowCfg& c, const BackArgs& a, hipStream_t st
 }
 
 template <int S, int G, int VEC, bool PAD>
-hipError_t launch_backward(const RowCfg& c, const BackArgs& a, hipStream_t st) {
+hipError_t launch_backward(const RowCfg& c, const BackArgs& a, hipStream_t st, const LaunchEvents*) {
     // the backward's blocks are the forward's row blocks (no selection bias)
     constexpr int NW = rows_waves(S, G, false);
     if (c.NW != NW) return hipErrorInvalidValue;
@@ -808,9 +811,9 @@ hipError_t launch_backward(const RowCfg& c, const BackArgs& a, hipStream_t st) {
 
 // Dispatch over (G, VEC, PAD) for one S.
 template <int S, typename ArgsT, template <int, int, bool> class Launch>
-hipError_t dispatch(const RowCfg& c, const ArgsT& a, hipStream_t st) {
+hipError_t dispatch(const RowCfg& c, const ArgsT& a, hipStream_t st, const LaunchEvents* ev) {
 #define MOE_CASE(GG, VV, PP) \
-    if (c.G == GG && c.VEC == VV && c.PAD == PP) return Launch<GG, VV, PP>::run(c, a, st);
+    if (c.G == GG && c.VEC == VV && c.PAD == PP) return Launch<GG, VV, PP>::run(c, a, st, ev);
     MOE_CASE(4, 4, 0) MOE_CASE(8, 4, 0) MOE_CASE(16, 4, 0) MOE_CASE(24, 4, 0)
     MOE_CASE(4, 4, 1) MOE_CASE(8, 4, 1) MOE_CASE(16, 4, 1) MOE_CASE(24, 4, 1)
     MOE_CASE(1, 1, 1) MOE_CASE(2, 1, 1) MOE_CASE(4, 1, 1) MOE_CASE(8, 1, 1)
@@ -825,24 +828,27 @@ hipError_t dispatch(const RowCfg& c, const ArgsT& a, hipStream_t st) {
     namespace {                                                                            \
     template <int G, int V, bool P>                                                        \
     struct RowsL {                                                                         \
-        static hipError_t run(const RowCfg& c, const RowsArgs& a, hipStream_t st) {        \
-            return rows_impl::launch_rows<SV, G, V, P>(c, a, st);                          \
+        static hipError_t run(const RowCfg& c, const RowsArgs& a, hipStream_t st,          \
+                              const LaunchEvents* ev) {                                    \
+            return rows_impl::launch_rows<SV, G, V, P>(c, a, st, ev);                      \
         }                                                                                  \
     };                                                                                     \
     template <int G, int V, bool P>                                                        \
     struct BackL {                                                                         \
-        static hipError_t run(const RowCfg& c, const BackArgs& a, hipStream_t st) {        \
-            return rows_impl::launch_backward<SV, G, V, P>(c, a, st);                      \
+        static hipError_t run(const RowCfg& c, const BackArgs& a, hipStream_t st,          \
+                              const LaunchEvents* ev) {                                    \
+            return rows_impl::launch_backward<SV, G, V, P>(c, a, st, ev);                  \
         }                                                                                  \
     };                                                                                     \
     }                                                                                      \
     template <>                                                                            \
-    hipError_t launch_rows_s<SV>(const RowCfg& c, const RowsArgs& a, hipStream_t st) {     \
-        return rows_impl::dispatch<SV, RowsArgs, RowsL>(c, a, st);                         \
+    hipError_t launch_rows_s<SV>(const RowCfg& c, const RowsArgs& a, hipStream_t st,       \
+                                 const LaunchEvents* ev) {                                 \
+        return rows_impl::dispatch<SV, RowsArgs, RowsL>(c, a, st, ev);                     \
     }                                                                                      \
     template <>                                                                            \
     hipError_t launch_backward_s<SV>(const RowCfg& c, const BackArgs& a, hipStream_t st) { \
-        return rows_impl::dispatch<SV, BackArgs, BackL>(c, a, st);                         \
+        return rows_impl::dispatch<SV, BackArgs, BackL>(c, a, st, nullptr);                \
     }
 
 }  // namespace moe
