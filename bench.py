@@ -417,7 +417,8 @@ def main():
 
     ab = alg_bytes(w, w.T)
     if gate_bwd:
-        dom_name, dom_bytes, dom_ms = "gate_backward_kernel", ab["gate_backward"], gb_ms
+        # events around the call: the product kernel and the dWg slice reduction
+        dom_name, dom_bytes, dom_ms = "gate_backward (product kernel + slice reduction)", ab["gate_backward"], gb_ms
     elif w.d > 0:
         dom_name, dom_bytes, dom_ms = "gate+route forward (no per-kernel split)", ab["forward"], ms_step
     elif w.backward and bwd_ms > rows_ms:
@@ -425,7 +426,8 @@ def main():
     else:
         dom_name, dom_bytes, dom_ms = "route_rows_kernel", ab["rows"], rows_ms
     if gate_bwd:  # the kernel the gate backward launches for this E (its reduce step aside)
-        traffic = measured_traffic(w.name, "moe::gate_backward_mfma_kernel" if w.E <= 16
+        traffic = measured_traffic(w.name, "moe::gate_backward_bf16_kernel" if w.E <= 8
+                                   else "moe::gate_backward_mfma_kernel" if w.E <= 16
                                    else "moe::gate_backward_kernel<")
     else:
         traffic = measured_traffic(w.name, dom_name) if w.d == 0 else None

@@ -5,8 +5,10 @@
 // dlogits is the routing gradient with respect to the logits.
 //
 // Both products stream X (or dX) once and are bound by HBM (about 6 flop per
-// byte), fused in one pass.  For E <= 16 both run on the matrix cores
-// (v_mfma_f32_16x16x4_f32, fp32 in and out).  dWg, the reduction over
+// byte), fused in one pass.  For E <= 8 both run on bf16 matrix cores with
+// dlogits split exactly into three bf16 parts (gate_backward_bf16_kernel,
+// below); for 8 < E <= 16 on fp32 matrix cores (v_mfma_f32_16x16x4_f32, fp32
+// in and out), as follows.  dWg, the reduction over
 // tokens: 16 lanes share a row, lane n of a row holds CPL consecutive
 // columns, and a step of four rows is, for each of the lane's CPL column
 // offsets q, the product of A = dlogits [16 experts x 4 rows] (lane l: row
@@ -346,6 +348,240 @@ gate_backward_mfma_kernel(const GateBackArgs a)
     }
 }
 
+// ---- E <= 8: both products on bf16 matrix cores.
+//
+// v_mfma_f32_16x16x32_bf16: lane l gives A[l%16][8(l/16) .. +8) and
+// B[8(l/16) .. +8)[l%16] and receives D[4(l/16) + i][l%16] in element i.
+// dlogits is fp32; each value v is split into three bf16 parts,
+// v = hi + mid + lo (hi: v rounded to bf16; mid: the remainder rounded; lo:
+// what is left, which a bf16 significand holds exactly), so each product of
+// a part with a bf16 operand is exact and both results are fp32 sums of the
+// exact products, as with fp32 operands.
+//   dX, per 16 rows and 16-column tile t: K = 32 holds (part, expert) pairs,
+//   8 per part (24 used).  A = Wg[col(t, m)][e] (the same for every part),
+//   B = part p of dlogits[row n][e]; with col(t, m) = 32(m/4) + 4t + m%4 lane
+//   l receives 32 consecutive columns of row l%16, staged through LDS so that
+//   each store writes whole runs of a row.
+//   dWg, per 32 rows of the wave and 16-column tile c: K = the rows.  A =
+//   X[row k][column m] from an LDS copy of the wave's X tile (row pitch 260
+//   bytes: the 64 lanes' 8-row column reads fall in distinct banks); B =
+//   parts of dlogits[row k][n%8] in the 16 columns n, hi for n < 8 and mid
+//   for n >= 8, then lo for n < 8 into the same accumulator; columns n and
+//   n + 8 are added at the end.
+constexpr int kB8Waves = 4;
+constexpr int kB8Cols = 128;               // columns per block
+constexpr int kB8Steps = 8;                // 4-row steps per wave iteration (32 rows)
+constexpr int kXPitch = kB8Cols * 2 + 4;   // bytes per staged X row
+constexpr int kDPitch = kB8Cols * 2 + 16;  // bytes per staged dX row
+constexpr int kB8Stage = 32 * kXPitch;     // the dX stage (16 rows) reuses the X tile's space
+static_assert(16 * kDPitch <= kB8Stage, "dX stage fits the X tile's space");
+constexpr int kDlPitch = 9;                // floats per staged dlogits row (distinct banks)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Exact three-way split of two values into bf16 pairs (element 0 = a).  A
+// non-finite value keeps itself as hi and zero parts below.
+__device__ __forceinline__ void split3(float a, float b, uint32_t& hi, uint32_t& mid, uint32_t& lo) {
+    const uint32_t h = pack_bf16x2(a, b);
+    const float ra = __builtin_isfinite(a) ? a - __uint_as_float(h << 16) : 0.f;
+    const float rb = __builtin_isfinite(b) ? b - __uint_as_float(h & 0xFFFF0000u) : 0.f;
+    const uint32_t m = pack_bf16x2(ra, rb);
+    hi = h;
+    mid = m;
+    lo = pack_bf16x2(ra - __uint_as_float(m << 16), rb - __uint_as_float(m & 0xFFFF0000u));
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+    return __builtin_bit_cast(bf16x8, make_uint4(w0, w1, w2, w3));
+}
+
+__global__ void __launch_bounds__(kB8Waves * 64) __attribute__((amdgpu_waves_per_eu(2)))
+gate_backward_bf16_kernel(const GateBackArgs a)
+{
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kB8Waves * kB8Stage];
+    __shared__ float dlt_all[kB8Waves][32 * kDlPitch];
+    __shared__ float wred[kB8Cols][8];
+    const int E = a.E, d = a.d;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15, r = lane >> 4;
+    const int cb = blockIdx.x * kB8Cols;  // the block's first column
+    const int colx = cb + 8 * n;          // the lane's 8 columns of an X row
+    const bool col_ok = colx < d;         // d % 8 == 0: all 8 in or all out
+    const long t0 = (long(blockIdx.y) * a.T) / gridDim.y;
+    const long t1 = (long(blockIdx.y + 1) * a.T) / gridDim.y;
+    unsigned char* stage = lds + wave * kB8Stage;
+    float* dlt = dlt_all[wave];  // dlogits of the wave's 32 rows: [k][e], pitch kDlPitch
+
+    // dX A operands: Wg[col(t, n)][0..8) for the parts r < 3, zero for r = 3
+    bf16x8 wa[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int c = cb + 32 * (n >> 2) + 4 * t + (n & 3);
+        uint32_t w[4] = {0u, 0u, 0u, 0u};
+        if (a.dX && r < 3 && c < d) {
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const uint32_t lo = (2 * h < E) ? a.Wg[long(c) * E + 2 * h] : 0u;
+                const uint32_t hi = (2 * h + 1 < E) ? a.Wg[long(c) * E + 2 * h + 1] : 0u;
+                w[h] = lo | (hi << 16);
+            }
+        }
+        wa[t] = as_bf16x8(w[0], w[1], w[2], w[3]);
+    }
+    f32x4 acc[8];  // dWg: tile c, column 16c + 4r + i, slot n
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // A wave's rows in one iteration: k = 4u + q is row s0 + u*step + q.
+    // Loads of the next iteration are in flight while this one computes.
+    const long step = 4L * kB8Waves;
+    const long S = step * kB8Steps;
+    uint4 xv[kB8Steps];
+    float dv[4];
+    auto load_iter = [&](long sb) {
+#pragma unroll
+        for (int u = 0; u < kB8Steps; ++u) {
+            const long row = sb + u * step + r;
+            const long rr = row < t1 ? row : t0;
+            xv[u] = col_ok ? *reinterpret_cast<const uint4*>(a.X + rr * d + colx) : make_uint4(0, 0, 0, 0);
+        }
+        // dlogits (k, e) for idx = lane + 64j: k = idx/8, e = idx%8; rows past
+        // the slice and padding experts are zero
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int idx = lane + 64 * j, k = idx >> 3, e = idx & 7;
+            const long row = sb + (k >> 2) * step + (k & 3);
+            dv[j] = (row < t1 && e < E) ? a.dlogits[row * E + e] : 0.f;
+        }
+    };
+    long s0 = t0 + 4L * wave;
+    if (s0 < t1) load_iter(s0);
+    for (; s0 < t1; s0 += S) {
+        if (a.dWg_part) {
+#pragma unroll
+            for (int u = 0; u < kB8Steps; ++u) {
+                uint32_t* dst = reinterpret_cast<uint32_t*>(stage + (4 * u + r) * kXPitch + 16 * n);
+                dst[0] = xv[u].x;
+                dst[1] = xv[u].y;
+                dst[2] = xv[u].z;
+                dst[3] = xv[u].w;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int idx = lane + 64 * j;
+            dlt[(idx >> 3) * kDlPitch + (idx & 7)] = dv[j];
+        }
+        wave_lds_sync();
+        if (s0 + S < t1) load_iter(s0 + S);
+
+        if (a.dWg_part) {
+            // B: rows k = 8r + i, expert n%8: hi|mid, then lo
+            uint32_t bh[4], bl[4];
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                uint32_t hi, mid, lo;
+                split3(dlt[(8 * r + 2 * h) * kDlPitch + (n & 7)], dlt[(8 * r + 2 * h + 1) * kDlPitch + (n & 7)],
+                       hi, mid, lo);
+                bh[h] = (n < 8) ? hi : mid;
+                bl[h] = (n < 8) ? lo : 0u;
+            }
+            const bf16x8 Bhm = as_bf16x8(bh[0], bh[1], bh[2], bh[3]);
+            const bf16x8 Blo = as_bf16x8(bl[0], bl[1], bl[2], bl[3]);
+            // A: X[8r + i][16c + n], i < 8; half the tiles' reads at a time,
+            // all issued before the first is used
+#pragma unroll
+            for (int c0 = 0; c0 < 8; c0 += 4) {
+                uint16_t xe[4][8];
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        xe[c][i] = *reinterpret_cast<const uint16_t*>(stage + (8 * r + i) * kXPitch +
+                                                                      2 * (16 * (c0 + c) + n));
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const bf16x8 A = as_bf16x8(uint32_t(xe[c][0]) | (uint32_t(xe[c][1]) << 16),
+                                               uint32_t(xe[c][2]) | (uint32_t(xe[c][3]) << 16),
+                                               uint32_t(xe[c][4]) | (uint32_t(xe[c][5]) << 16),
+                                               uint32_t(xe[c][6]) | (uint32_t(xe[c][7]) << 16));
+                    acc[c0 + c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bhm, acc[c0 + c], 0, 0, 0);
+                    acc[c0 + c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Blo, acc[c0 + c], 0, 0, 0);
+                }
+            }
+        }
+        wave_lds_sync();  // the dX stage reuses the X tile's space
+        if (a.dX) {
+#pragma unroll
+            for (int G = 0; G < 2; ++G) {
+                // B: part r of dlogits[row 16G + n][0..8), zero for r = 3
+                const float* g = dlt + (16 * G + n) * kDlPitch;
+                uint32_t b[4];
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    uint32_t hi, mid, lo;
+                    split3(g[2 * h], g[2 * h + 1], hi, mid, lo);
+                    b[h] = (r == 0) ? hi : (r == 1) ? mid : (r == 2) ? lo : 0u;
+                }
+                const bf16x8 B = as_bf16x8(b[0], b[1], b[2], b[3]);
+                f32x4 o[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t)
+                    o[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[t], B, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                uint32_t pk[16];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) {
+                    pk[2 * t] = pack_bf16x2(o[t][0], o[t][1]);
+                    pk[2 * t + 1] = pack_bf16x2(o[t][2], o[t][3]);
+                }
+                // row n of the group, block columns 32r .. 32r + 32
+#pragma unroll
+                for (int w = 0; w < 4; ++w)
+                    *reinterpret_cast<uint4*>(stage + n * kDPitch + 64 * r + 16 * w) =
+                        make_uint4(pk[4 * w], pk[4 * w + 1], pk[4 * w + 2], pk[4 * w + 3]);
+                wave_lds_sync();
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const long row = s0 + (4 * G + q) * step + r;
+                    if (col_ok && row < t1) {
+                        // nontemporal: dX is not read again here, and written-back
+                        // lines would otherwise stall the next kernel's reads
+                        const u32x4 v = *reinterpret_cast<const u32x4*>(stage + (4 * q + r) * kDPitch + 16 * n);
+                        __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(a.dX + row * d + colx));
+                    }
+                }
+                wave_lds_sync();
+            }
+        }
+    }
+
+    if (!a.dWg_part) return;
+    // slots n and n + 8 hold parts of the same expert; then the waves in
+    // order through LDS
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[c][i] += __shfl_xor(acc[c][i], 8);
+    for (int w = 0; w < kB8Waves; ++w) {
+        if (wave == w && n < 8) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float& slot = wred[16 * c + 4 * r + i][n];
+                    slot = (w == 0) ? acc[c][i] : slot + acc[c][i];
+                }
+        }
+        __syncthreads();
+    }
+    float* part = a.dWg_part + long(blockIdx.y) * d * E;
+    for (int i = threadIdx.x; i < kB8Cols * E; i += kB8Waves * 64) {
+        const int cc = i / E, e = i - (i / E) * E;
+        const int col = cb + cc;
+        if (col < d) part[long(col) * E + e] = wred[cc][e];
+    }
+}
+
 // dWg[i] = sum over the token slices of part[slice][i], slices in order
 // (eight loads in flight at a time, the additions still in slice order).
 __global__ void __launch_bounds__(256)
@@ -392,7 +628,7 @@ hipError_t launch_gate_backward(const GateBackArgs& a, hipStream_t st) {
     const dim3 grid((a.d + tile - 1) / tile, slices);
     GateBackArgs b = a;
     if (!a.dWg) b.dWg_part = nullptr;
-    if (a.E <= 8) hipLaunchKernelGGL((gate_backward_mfma_kernel<8, 8>), grid, dim3(kMfWaves * 64), 0, st, b);
+    if (a.E <= 8) hipLaunchKernelGGL(gate_backward_bf16_kernel, grid, dim3(kB8Waves * 64), 0, st, b);
     else if (a.E <= 16) hipLaunchKernelGGL((gate_backward_mfma_kernel<16, 4>), grid, dim3(kMfWaves * 64), 0, st, b);
     else if (a.E <= 32) hipLaunchKernelGGL(gate_backward_kernel<2>, grid, dim3(kGbThreads), 0, st, b);
     else if (a.E <= 64) hipLaunchKernelGGL(gate_backward_kernel<1>, grid, dim3(kGbThreads), 0, st, b);
