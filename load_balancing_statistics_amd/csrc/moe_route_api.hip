@@ -215,6 +215,10 @@ int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
     ca.split_P = ws.split_P;
     ca.cnt_part = ws.cnt_part; ca.P_part = ws.P_part; ca.flag_part = ws.flag_part;
     ca.fold_q = fold_q; ca.B = c.B; ca.nw = scat_nw;
+    // few row blocks: the statistics get workgroups of their own, so that no
+    // block adds them to its share of the permutation
+    ca.stats_sep = (c.B + p->n_micro <= moe::kAssumedCUs) ? 1 : 0;
+    ca.n_micro = p->n_micro;
     ca.alpha = p->alpha;
     ca.p_masked = (p->flags & MOE_P_MASKED) ? 1 : 0;
     ca.counts = out->counts; ca.offsets = out->offsets; ca.f = out->f; ca.P = out->P;

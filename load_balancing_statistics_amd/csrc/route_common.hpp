@@ -222,6 +222,8 @@ struct ScatterArgs {
     const float* P_part;
     const int32_t* flag_part;
     int fold_q;  // > 0: sum the row pass's partials here, in fold_q groups of row blocks
+    int stats_sep;  // 1: n_micro extra workgroups form the statistics (B + n_micro fit the chip)
+    int n_micro;
     int nw;      // waves per block (scatter_waves)
     int B;       // row blocks in total
     int T, E, k, Tm, bpm, nsplit;

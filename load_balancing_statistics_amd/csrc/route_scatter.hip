@@ -11,7 +11,9 @@
 // offsets being the exclusive prefix sum, in expert order, of the
 // microbatch's counts (the sums of its split counts), which every block
 // forms for itself.  The first block of each microbatch also writes the
-// counts, the offsets and the balance statistics.
+// counts, the offsets and the balance statistics -- or, when the row blocks
+// and one more workgroup per microbatch fit the chip at once, that extra
+// workgroup does, so that no block adds them to its share of the rows.
 //
 // A token picks an expert at most once (its top-k are distinct), so inside an
 // expert the (t, j) order is the token order.  The block walks its rows in
@@ -163,8 +165,8 @@ __device__ void block_excl_scan(const int* v, int n, int* out, int* wsum) {
 // so consecutive logical blocks -- whose runs of each expert are adjacent in
 // the permutation -- are given to workgroups of one XCD, and the partial
 // cache lines they share meet in one L2.
-__device__ __forceinline__ int logical_block() {
-    const int n = gridDim.x, b = blockIdx.x;
+__device__ __forceinline__ int logical_block(int n) {
+    const int b = blockIdx.x;
     return (n % 8 == 0) ? (b % 8) * (n / 8) + b / 8 : b;
 }
 
@@ -191,7 +193,10 @@ route_scatter_kernel(const ScatterArgs a)
     __shared__ int wsum[kScatMaxWaves];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int b = logical_block();
+    // With stats_sep, workgroups B .. B + n_micro - 1 only form their
+    // microbatch's offsets and statistics (as its first row block would).
+    const bool stats_only = a.stats_sep && int(blockIdx.x) >= a.B;
+    const int b = stats_only ? (int(blockIdx.x) - a.B) * a.bpm : logical_block(a.B);
     const int mb = b / a.bpm, bi = b - mb * a.bpm;
     const int my_split = bi / (kScanWaves * kScanPerWave);
     long row_begin, row_end;
@@ -236,12 +241,12 @@ route_scatter_kernel(const ScatterArgs a)
                 ev[u] = load_or(a.topk_idx, i0 + u, active && u < KC && g * KC + u < k, -1);
         }
     };
-    load_window(row_begin);
+    if (!stats_only) load_window(row_begin);
     // per expert: the microbatch's count tot[e], this block's start relative
     // to the expert's offset base[e] (the count in the microbatch's earlier
     // row blocks) and, for the statistics, the probability sum psum
     constexpr int EPT = (MOE_ROUTE_MAX_E + NW * 64 - 1) / (NW * 64);  // experts per thread
-    const bool stats_block = bi == 0;
+    const bool stats_block = a.stats_sep ? stats_only : bi == 0;
     double psum[EPT];
 #pragma unroll
     for (int it = 0; it < EPT; ++it) psum[it] = 0.0;
@@ -282,9 +287,10 @@ route_scatter_kernel(const ScatterArgs a)
             ftot[t] = tt;
             fps[t] = ps;
         }
-        // status: the flags of every row block, by logical block 0 (the row
-        // pass zeroed the word; the scatter only ORs bits into it)
-        if (a.status && b == 0) {
+        // status: the flags of every row block, by logical block 0 or, with
+        // statistics workgroups, by the first of them (the row pass zeroed
+        // the word; the scatter only ORs bits into it)
+        if (a.status && b == 0 && (stats_only || !a.stats_sep)) {
             int fl = 0;
             for (int j = tid; j < a.B; j += NW * 64) fl |= a.flag_part[j];
             if (__syncthreads_or(fl & MOE_STATUS_NONFINITE) && tid == 0)
@@ -355,6 +361,7 @@ route_scatter_kernel(const ScatterArgs a)
     // tot and lofs are reused by the windows only after their first
     // barrier; the row masks' LDS is free until the first window
     if (stats_block) microbatch_statistics<NW, EPT>(a, mb, tot, lofs, psum, reinterpret_cast<double*>(gm));
+    if (stats_only) return;
 
     uint64_t* mym = gm + wave * E;
     const int* mypre = wpre + wave * E;
@@ -480,7 +487,7 @@ hipError_t launch_scatter_nw(const RowCfg& c, const ScatterArgs& a, size_t lds, 
                                            hipFuncAttributeMaxDynamicSharedMemorySize, int(lds));
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(route_scatter_kernel<NW>, dim3(c.B), dim3(NW * 64), lds, st, a);
+    hipLaunchKernelGGL(route_scatter_kernel<NW>, dim3(c.B + (a.stats_sep ? a.n_micro : 0)), dim3(NW * 64), lds, st, a);
     return hipGetLastError();
 }
 
