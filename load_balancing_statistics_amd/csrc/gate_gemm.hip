@@ -16,8 +16,11 @@
 // its tile of X coalesced (16 lanes cover 256 contiguous bytes of a row),
 // stores it in LDS (row pitch 272 bytes: the 16 rows an MFMA operand read
 // touches fall in distinct banks) and reads the operands back from there.
-// Operand B is laid out once per call by a tiny kernel, Wb[step][tile][lane]
-// (16 bytes each, zero past d and E), so its loads are contiguous per wave.
+// Operand B: when E % 8 == 0 each wave loads its chunk's slice of Wg (a
+// contiguous run) beside X and writes it transposed into LDS, from where the
+// operands are 16-byte reads; otherwise a tiny kernel lays B out once per
+// call, Wb[step][tile][lane] (16 bytes each, zero past d and E), so that its
+// loads are contiguous per wave.
 //
 // A block computes 32 tokens (two 16-token tiles); its 4 waves split the k
 // range into four contiguous quarters, staging 128 k (256 bytes per row) at a
@@ -72,14 +75,23 @@ __device__ __forceinline__ void wave_lds_sync() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int NT>
+// RAW (E % 8 == 0): a wave reads its chunk's slice of Wg itself -- rows
+// 128c .. 128c + 127 of [d, E], one contiguous run of 128E values -- with
+// 16-byte loads issued beside its X loads, and writes it transposed into LDS
+// (expert rows, pitch kRowPitch, the padding experts zero), from which it
+// reads the B operands as 16-byte runs of 8 k.  Otherwise the B operands
+// come pre-laid-out from Wb (swizzle_wg_kernel).
+template <int NT, bool RAW>
 __global__ void __launch_bounds__(kGateWaves * 64)
-gate_gemm_kernel(const uint16_t* __restrict__ X, const uint4* __restrict__ Wb,
+gate_gemm_kernel(const uint16_t* __restrict__ X, const uint4* __restrict__ Wb, const uint16_t* __restrict__ Wg,
                  float* __restrict__ logits, int T, int d, int E)
 {
     constexpr int kStage = kRows * kRowPitch;
+    constexpr int kWbT = RAW ? 16 * NT * kRowPitch : 0;
+    constexpr int kWave = kStage + kWbT;
     constexpr int kRed = kGateWaves * kMT * NT * 64 * 16;
-    constexpr int kLds = kGateWaves * kStage > kRed ? kGateWaves * kStage : kRed;
+    constexpr int kLds = kGateWaves * kWave > kRed ? kGateWaves * kWave : kRed;
+    constexpr int kPieces = 4 * NT;  // 16-byte pieces of the Wg slice a lane loads (E/4 used)
     __shared__ __attribute__((aligned(16))) unsigned char lds[kLds];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int r16 = lane & 15, kq = lane >> 4;
@@ -87,7 +99,8 @@ gate_gemm_kernel(const uint16_t* __restrict__ X, const uint4* __restrict__ Wb,
     const int nchunks = (d + kChunkK - 1) / kChunkK;
     const int per = (nchunks + kGateWaves - 1) / kGateWaves;
     const int c0 = min(wave * per, nchunks), c1 = min(c0 + per, nchunks);
-    unsigned char* stage = lds + wave * kStage;
+    unsigned char* stage = lds + wave * kWave;
+    unsigned char* wbt = stage + kStage;
 
     f32x4 acc[kMT][NT];
 #pragma unroll
@@ -95,9 +108,17 @@ gate_gemm_kernel(const uint16_t* __restrict__ X, const uint4* __restrict__ Wb,
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[m][t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    if constexpr (RAW) {
+        // the padding experts' rows stay zero
+        for (int e = E; e < 16 * NT; ++e)
+            for (int q = lane; q < kChunkK / 2; q += 64)
+                reinterpret_cast<uint32_t*>(wbt + e * kRowPitch)[q] = 0u;
+    }
+
     // coalesced loads: load j covers rows kRowsPerLoad*j + lr, lane's 8 k at lc
     const int lr = lane / kLanesPerRow, lc = (lane % kLanesPerRow) * 8;
     uint4 xr[kLoads];
+    uint4 wr[kPieces];
     auto load_chunk = [&](int c) {
         const int k = c * kChunkK + lc;  // d % 8 == 0: the lane's 8 k are all in or all out
 #pragma unroll
@@ -106,19 +127,56 @@ gate_gemm_kernel(const uint16_t* __restrict__ X, const uint4* __restrict__ Wb,
             xr[j] = (row < T && k < d) ? *reinterpret_cast<const uint4*>(X + row * d + k)
                                        : make_uint4(0, 0, 0, 0);
         }
+        if constexpr (RAW) {
+            // lane covers values [2E*lane, 2E*lane + 2E) of the slice: E/4 pieces
+            // of 8 values, each 8 experts of one k row (E % 8 == 0)
+#pragma unroll
+            for (int j = 0; j < kPieces; ++j) {
+                const int i = 2 * E * lane + 8 * j;  // value index within the slice
+                const int kk = c * kChunkK + i / E;
+                wr[j] = (4 * j < E && kk < d) ? *reinterpret_cast<const uint4*>(Wg + long(c) * kChunkK * E + i)
+                                              : make_uint4(0, 0, 0, 0);
+            }
+        }
     };
     if (c0 < c1) load_chunk(c0);
     for (int c = c0; c < c1; ++c) {
         uint4 bv[kSteps][NT];
+        if constexpr (!RAW) {
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s)
+            for (int s = 0; s < kSteps; ++s)
 #pragma unroll
-            for (int t = 0; t < NT; ++t) bv[s][t] = Wb[(long(c * kSteps + s) * NT + t) * 64 + lane];
+                for (int t = 0; t < NT; ++t) bv[s][t] = Wb[(long(c * kSteps + s) * NT + t) * 64 + lane];
+        }
 #pragma unroll
         for (int j = 0; j < kLoads; ++j)
             *reinterpret_cast<uint4*>(stage + (kRowsPerLoad * j + lr) * kRowPitch + (lane % kLanesPerRow) * 16) = xr[j];
+        if constexpr (RAW) {
+            // transpose: value (k, e) to row e, column k
+#pragma unroll
+            for (int j = 0; j < kPieces; ++j) {
+                if (4 * j < E) {
+                    const int i = 2 * E * lane + 8 * j;
+                    const int kr = i / E, e0 = i - kr * E;
+                    uint16_t* col = reinterpret_cast<uint16_t*>(wbt + e0 * kRowPitch) + kr;
+                    const uint32_t w4[4] = {wr[j].x, wr[j].y, wr[j].z, wr[j].w};
+#pragma unroll
+                    for (int h = 0; h < 4; ++h) {
+                        col[(2 * h) * (kRowPitch / 2)] = uint16_t(w4[h]);
+                        col[(2 * h + 1) * (kRowPitch / 2)] = uint16_t(w4[h] >> 16);
+                    }
+                }
+            }
+        }
         wave_lds_sync();
         if (c + 1 < c1) load_chunk(c + 1);  // in flight while this chunk is multiplied
+        if constexpr (RAW) {
+#pragma unroll
+            for (int s = 0; s < kSteps; ++s)
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+                    bv[s][t] = *reinterpret_cast<const uint4*>(wbt + (16 * t + r16) * kRowPitch + 64 * s + 16 * kq);
+        }
 #pragma unroll
         for (int s = 0; s < kSteps; ++s)
 #pragma unroll
@@ -172,20 +230,27 @@ size_t gate_workspace_bytes(int d, int E) { return align_up(size_t(gate_wb_units
 
 hipError_t launch_gate_gemm(const GateArgs& a, uint16_t* wt, hipStream_t st) {
     const int nt = gate_tiles_n(a.E);
-    const long n = gate_wb_units(a.d, a.E);
-    uint4* wb = reinterpret_cast<uint4*>(wt);
-    const int tb = int(std::min<long>((n + 255) / 256, 1024));
-    hipLaunchKernelGGL(swizzle_wg_kernel, dim3(tb), dim3(256), 0, st, a.Wg, wb, a.d, a.E, nt, n);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     const dim3 grid((a.T + kRows - 1) / kRows);
+    uint4* wb = reinterpret_cast<uint4*>(wt);
+    const bool raw = a.E % 8 == 0;
+    if (!raw) {
+        const long n = gate_wb_units(a.d, a.E);
+        const int tb = int(std::min<long>((n + 255) / 256, 1024));
+        hipLaunchKernelGGL(swizzle_wg_kernel, dim3(tb), dim3(256), 0, st, a.Wg, wb, a.d, a.E, nt, n);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+#define MOE_GEMM(NTV)                                                                                  \
+    if (raw) hipLaunchKernelGGL((gate_gemm_kernel<NTV, true>), grid, dim3(256), 0, st, a.X, wb, a.Wg, a.logits, a.T, a.d, a.E); \
+    else hipLaunchKernelGGL((gate_gemm_kernel<NTV, false>), grid, dim3(256), 0, st, a.X, wb, a.Wg, a.logits, a.T, a.d, a.E);
     switch (nt) {
-        case 1: hipLaunchKernelGGL(gate_gemm_kernel<1>, grid, dim3(256), 0, st, a.X, wb, a.logits, a.T, a.d, a.E); break;
-        case 2: hipLaunchKernelGGL(gate_gemm_kernel<2>, grid, dim3(256), 0, st, a.X, wb, a.logits, a.T, a.d, a.E); break;
-        case 3: hipLaunchKernelGGL(gate_gemm_kernel<3>, grid, dim3(256), 0, st, a.X, wb, a.logits, a.T, a.d, a.E); break;
-        case 4: hipLaunchKernelGGL(gate_gemm_kernel<4>, grid, dim3(256), 0, st, a.X, wb, a.logits, a.T, a.d, a.E); break;
+        case 1: MOE_GEMM(1) break;
+        case 2: MOE_GEMM(2) break;
+        case 3: MOE_GEMM(3) break;
+        case 4: MOE_GEMM(4) break;
         default: return hipErrorInvalidValue;
     }
+#undef MOE_GEMM
     return hipGetLastError();
 }
 

@@ -130,11 +130,13 @@ def test_gate_small():
 
 
 @pytest.mark.parametrize("T,d,E", [(1003, 520, 8), (77, 4096, 16), (130, 264, 12), (1000, 512, 40),
-                                   (1, 8, 1)])
+                                   (1, 8, 1), (300, 392, 64), (65, 136, 24)])
 def test_gate_logits_shapes(T, d, E):
     """Gate GEMM alone over ragged shapes: T not a multiple of the 64-token
-    block, d not a multiple of 32, E = 16 (full tile), E = 40 (three expert
-    tiles, the wide kernel), a single token and a single 8-wide k step."""
+    block, d not a multiple of 32 (nor of the 128-wide k chunk), E = 16 (full
+    tile), E = 40 and 64 (three and four expert tiles), E = 12 and 1 (weights
+    laid out by the small kernel, E % 8 != 0), a single token and a single
+    8-wide k step."""
     print(f"case gate_logits T={T} d={d} E={E}", flush=True)
     rng = np.random.default_rng(T + d + E)
     f32 = rng.standard_normal((T, d)).astype(np.float32)
