@@ -37,14 +37,15 @@ int check_shape(const moe_route_params* p) {
     if (p->flags & ~kKnownFlags) return MOE_ERR_INVALID_ARG;
     if (p->d > 0 && !moe::gate_supported(p->T, p->d, p->E)) return MOE_ERR_UNSUPPORTED;
     const bool bias = (p->flags & MOE_SELECT_BIAS) != 0;
-    const RowCfg c = moe::choose_rows(p->T, p->E, p->k, p->n_micro, bias);
+    const RowCfg c = moe::choose_rows(p->T, p->E, p->k, p->n_micro, bias, (p->flags & MOE_P_MASKED) != 0);
     if (c.G < 0 || moe::rows_lds_bytes(c, p->E, p->k, bias) > kMaxLds) return MOE_ERR_UNSUPPORTED;
     if (moe::scatter_lds_bytes(p->E, p->k, moe::scatter_waves(p->E, c.NW)) > kMaxLds) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
 RowCfg cfg_of(const moe_route_params* p) {
-    return moe::choose_rows(p->T, p->E, p->k, p->n_micro, (p->flags & MOE_SELECT_BIAS) != 0);
+    return moe::choose_rows(p->T, p->E, p->k, p->n_micro, (p->flags & MOE_SELECT_BIAS) != 0,
+                            (p->flags & MOE_P_MASKED) != 0);
 }
 
 // Capacity of page mhpq.cn/news/998159 section 4.5: the per-expert share of

@@ -42,13 +42,22 @@ constexpr int kAssumedCUs = 256;   // MI355X compute units (grid sizing only)
 // half the rows: the combine and the scatter that follow work per row
 // block, and the scatter's smaller blocks overlap two per compute unit;
 // measured 1.5 us less a step at E=256 top-8 than one block of 16), 12 in
-// one block when a lane owns 24.  The selection-bias variant keeps G more
-// registers per lane: 12 waves when a lane owns up to 16 columns, 8 when it
-// owns 24.  One or two lanes per row with 16 columns hold more per-row state
-// per lane (ranking passes): 12 waves there too, so nothing spills.
-constexpr int rows_waves(int S, int G, bool bias) {
-    return bias ? ((G > 16) ? 8 : 12) : ((G > 16 || (S <= 2 && G >= 16)) ? 12 : 8);
+// one block when a lane owns 24.  One or two lanes per row with 16 columns
+// hold more per-row state per lane (ranking passes): 12 waves there too, so
+// nothing spills.  The selection-bias variant reads the bias of its columns
+// from the block's LDS copy; it runs the two blocks of 8 as well when it fits
+// their register budget (whole rows of vector loads, all-token P: v3 shape
+// with a bias 38.7 -> 35.3 us against one block of 12), else one block of 12
+// (8 when a lane owns 24).
+constexpr int rows_waves(int S, int G, bool bias, bool masked = false, int vec = 4, bool pad = false) {
+    if (!bias) return (G > 16 || (S <= 2 && G >= 16)) ? 12 : 8;
+    if (G > 16) return 8;
+    return (!masked && vec == 4 && !pad && !(S <= 2 && G >= 16)) ? 8 : 12;
 }
+
+// Row-pass blocks per compute unit: two for the eight-wave blocks of lanes
+// owning up to 16 columns, else one.
+constexpr int rows_blocks_per_cu(int NW, int G) { return (NW == 8 && G <= 16) ? 2 : 1; }
 
 inline int next_pow2(int v) {
     int p = 1;
@@ -63,7 +72,7 @@ inline int next_pow2(int v) {
 // per block and the rows per block: one or two resident blocks per compute
 // unit over the whole batch, so the grid is one wave of blocks and the
 // per-block partials stay few.
-inline RowCfg choose_rows(int T, int E, int k, int n_micro, bool bias = false) {
+inline RowCfg choose_rows(int T, int E, int k, int n_micro, bool bias = false, bool masked = false) {
     RowCfg c{};
     c.VEC = (E % 4 == 0) ? 4 : 1;
     int S = next_pow2(k < 1 ? 1 : k);
@@ -78,11 +87,11 @@ inline RowCfg choose_rows(int T, int E, int k, int n_micro, bool bias = false) {
     }
     // unaligned rows take the generic (bounds-checked) column path
     c.PAD = (S * c.G != E || c.VEC == 1) ? 1 : 0;
-    c.NW = rows_waves(S, c.G, bias);
+    c.NW = rows_waves(S, c.G, bias, masked, c.VEC, c.PAD != 0);
     const int W = 64 / S;
     const long per_iter = long(c.NW) * W;
     const long Tm = T / n_micro;
-    const long blocks_per_cu = (!bias && c.NW == 8) ? 2 : 1;
+    const long blocks_per_cu = rows_blocks_per_cu(c.NW, c.G);
     const long target = kAssumedCUs * blocks_per_cu;
     // balanced split: every block of a microbatch gets floor or ceil of
     // Tm / bpm rows, at least one row group per wave iteration

@@ -14,10 +14,11 @@
 //     per-expert sums of softmax probabilities, used for f_i and P_i.
 // With a selection bias (BIAS; page mhpq.cn/news/998159 section 4.3) the
 // experts are ranked by the fp32 sums l + b_e while the softmax, the weights
-// and the probability sums use l: each lane keeps the bias of its columns in
-// registers (threshold and candidate mask) and the block keeps a copy in LDS
-// (candidate keys); the LDS row copy stays unbiased, so a winner's weight
-// is read from it exactly.
+// and the probability sums use l: the block keeps a copy of the bias in LDS,
+// from which each lane reads the bias of its columns for every row
+// (threshold and candidate mask; registers it would otherwise hold for the
+// whole pass) and the candidates theirs (keys); the LDS row copy stays
+// unbiased, so a winner's weight is read from it exactly.
 //
 // Top-k without sorting.  Lane s of a segment owns G columns.  The k-th
 // largest of the S lane maxima, tau, is a lower bound of the row's k-th
@@ -195,10 +196,18 @@ struct RowPass {
     __device__ __forceinline__ static void process(
         const RowsArgs& a, const float (&x)[G], long row, bool valid, int s,
         float* rowbuf, uint64_t* cand, int* hist, float (&acc)[G], int& bad,
-        int* queue, int& qn, long row_begin, const float (&bz)[G], const float* blds,
+        int* queue, int& qn, long row_begin, const float* blds,
         uint64_t* sel)
     {
         const int E = a.E, k = a.k;
+        // the bias of the lane's columns, from the block's LDS copy (0 for
+        // padding columns; unused without BIAS)
+        float bz[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int col = col_of<S, VEC>(g, s);
+            bz[g] = (BIAS && (!PAD || col < E)) ? blds[col] : 0.f;
+        }
         // ---- row maximum (softmax) and the candidate threshold tau
         // (selection values: the logits, or the biased logits)
         float lmax = x[0];
@@ -454,14 +463,14 @@ struct RowPass {
 
 // Waves per SIMD the row pass must fit: 4 for the eight-wave blocks that run
 // two per compute unit (128 registers, as one block of 16 had), else 1.
-template <int NW, bool BIAS>
-constexpr int rows_min_waves_per_simd() { return (NW == 8 && !BIAS) ? 4 : 1; }
+template <int NW, int G>
+constexpr int rows_min_waves_per_simd() { return rows_blocks_per_cu(NW, G) == 2 ? 4 : 1; }
 
 // MASKED: P from each token's picks only (flag MOE_P_MASKED), a compile-time
 // variant so that the all-token kernels keep their register budget.
 template <int S, int G, int VEC, bool PAD, int NW, bool BIAS, bool MASKED>
 __global__ void __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(rows_min_waves_per_simd<NW, BIAS>())))
+__attribute__((amdgpu_waves_per_eu(rows_min_waves_per_simd<NW, G>())))
 route_rows_kernel(const RowsArgs a)
 {
     using RP = RowPass<S, G, VEC, PAD, NW, BIAS, MASKED>;
@@ -500,18 +509,6 @@ route_rows_kernel(const RowsArgs a)
 #pragma unroll
     for (int g = 0; g < G; ++g) acc[g] = 0.f;
     int bad = 0;
-    // bias of the lane's columns (0 for padding columns; unused without BIAS)
-    float bz[G];
-#pragma unroll
-    for (int g = 0; g < G; ++g) bz[g] = 0.f;
-    if constexpr (BIAS) {
-#pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const int col = col_of<S, VEC>(g, s);
-            if (!PAD || col < E) bz[g] = a.bias[col];
-        }
-    }
-
     const long per_iter = long(NW) * W;
     const int iters = int((row_end - row_begin + per_iter - 1) / per_iter);
     const long row0 = row_begin + long(wave) * W + seg;
@@ -537,18 +534,18 @@ route_rows_kernel(const RowsArgs a)
     for (; it + 2 < iters; it += 2) {
         if (second && it >= cut && it < cut + 2) __builtin_amdgcn_s_setprio(0);
         load_row<S, G, VEC, PAD>(xb, a.logits, clamp(row_at(it + 1)), E, s);
-        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin, bz, blds, sel);
+        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin, blds, sel);
         load_row<S, G, VEC, PAD>(xa, a.logits, clamp(row_at(it + 2)), E, s);
         RP::process(a, xb, row_at(it + 1), row_at(it + 1) < row_end, s, rowbuf, cand, hist,
-                    acc, bad, queue, qn, row_begin, bz, blds, sel);
+                    acc, bad, queue, qn, row_begin, blds, sel);
     }
     if (it + 1 < iters) {
         load_row<S, G, VEC, PAD>(xb, a.logits, clamp(row_at(it + 1)), E, s);
-        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin, bz, blds, sel);
+        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin, blds, sel);
         RP::process(a, xb, row_at(it + 1), row_at(it + 1) < row_end, s, rowbuf, cand, hist,
-                    acc, bad, queue, qn, row_begin, bz, blds, sel);
+                    acc, bad, queue, qn, row_begin, blds, sel);
     } else if (it < iters) {
-        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin, bz, blds, sel);
+        RP::process(a, xa, row_at(it), row_at(it) < row_end, s, rowbuf, cand, hist, acc, bad, queue, qn, row_begin, blds, sel);
     }
 
     if (__builtin_expect(qn > 0, 0))
@@ -761,7 +758,7 @@ route_backward_kernel(const BackArgs a)
 
 template <int S, int G, int VEC, bool PAD, bool BIAS, bool MASKED>
 hipError_t launch_rows_v(const RowCfg& c, const RowsArgs& a, hipStream_t st, const LaunchEvents* ev) {
-    constexpr int NW = rows_waves(S, G, BIAS);
+    constexpr int NW = rows_waves(S, G, BIAS, MASKED, VEC, PAD);
     if (c.NW != NW) return hipErrorInvalidValue;
     const size_t lds = rows_lds_bytes(c, a.E, a.k, BIAS);
     auto kern = route_rows_kernel<S, G, VEC, PAD, NW, BIAS, MASKED>;
