@@ -44,13 +44,18 @@ constexpr int kAssumedCUs = 256;   // MI355X compute units (grid sizing only)
 // measured 1.5 us less a step at E=256 top-8 than one block of 16), 12 in
 // one block when a lane owns 24.  One or two lanes per row with 16 columns
 // hold more per-row state per lane (ranking passes): 12 waves there too, so
-// nothing spills.  The selection-bias variant reads the bias of its columns
+// nothing spills; likewise 16 columns of scalar loads (E not a multiple of
+// 4), whose kernels spill at the 128-register budget of two blocks of 8
+// (E = 250 top-8: 61 -> 55.5 us a call, 140 -> 105 us with masked P; kernels
+// of vector loads that spill stay faster as two blocks: E = 60 top-2 with
+// masked P 28.2 against 30.2 us as one block of 12).  The
+// selection-bias variant reads the bias of its columns
 // from the block's LDS copy; it runs the two blocks of 8 as well when it fits
 // their register budget (whole rows of vector loads, all-token P: v3 shape
 // with a bias 38.7 -> 35.3 us against one block of 12), else one block of 12
 // (8 when a lane owns 24).
 constexpr int rows_waves(int S, int G, bool bias, bool masked = false, int vec = 4, bool pad = false) {
-    if (!bias) return (G > 16 || (S <= 2 && G >= 16)) ? 12 : 8;
+    if (!bias) return (G > 16 || (S <= 2 && G >= 16) || (vec == 1 && G >= 16)) ? 12 : 8;
     if (G > 16) return 8;
     return (!masked && vec == 4 && !pad && !(S <= 2 && G >= 16)) ? 8 : 12;
 }

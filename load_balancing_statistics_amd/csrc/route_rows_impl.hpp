@@ -799,7 +799,7 @@ hipError_t launch_backward_nw(const RowCfg& c, const BackArgs& a, hipStream_t st
 template <int S, int G, int VEC, bool PAD>
 hipError_t launch_backward(const RowCfg& c, const BackArgs& a, hipStream_t st, const LaunchEvents*) {
     // the backward's blocks are the forward's row blocks (no selection bias)
-    constexpr int NW = rows_waves(S, G, false);
+    constexpr int NW = rows_waves(S, G, false, false, VEC);
     if (c.NW != NW) return hipErrorInvalidValue;
     const bool sp = a.p_masked || a.d_topk_w;
     return sp ? launch_backward_nw<S, G, VEC, PAD, NW, true>(c, a, st)
