@@ -195,6 +195,11 @@ EDGE = [
     (2500, 20, 1, 1, 1.05, -1, False, "normal"),
     (2048, 24, 1, 1, 1.0, -1, False, "quantized"),
     (1000, 13, 2, 1, 1.3, -1, True, "normal"),
+    # few row blocks in all: the statistics in workgroups of their own, with
+    # the split combine kernel (64 row blocks a microbatch) and without it
+    (32768, 8, 2, 2, 1.25, -1, True, "normal"),
+    (16384, 16, 4, 4, 1.0, -1, True, "quantized"),
+    (6000, 64, 2, 3, 1.1, -1, False, "normal"),
 ]
 
 
