@@ -96,7 +96,12 @@ inline RowCfg choose_rows(int T, int E, int k, int n_micro, bool bias = false, b
     const int W = 64 / S;
     const long per_iter = long(c.NW) * W;
     const long Tm = T / n_micro;
-    const long blocks_per_cu = rows_blocks_per_cu(c.NW, c.G);
+    long blocks_per_cu = rows_blocks_per_cu(c.NW, c.G);
+    // when two blocks per compute unit would leave each wave one row group,
+    // one block with two: the same rows in flight, half the row blocks for
+    // the combine and the scatter (65536 tokens, E=64 top-2: step 20.45 ->
+    // 20.0 us)
+    if (blocks_per_cu == 2 && long(T) <= 2L * kAssumedCUs * per_iter) blocks_per_cu = 1;
     const long target = kAssumedCUs * blocks_per_cu;
     // balanced split: every block of a microbatch gets floor or ceil of
     // Tm / bpm rows, at least one row group per wave iteration
