@@ -60,9 +60,8 @@ constexpr int rows_waves(int S, int G, bool bias, bool masked = false, int vec =
     return (!masked && vec == 4 && !pad && !(S <= 2 && G >= 16)) ? 8 : 12;
 }
 
-// Row-pass blocks per compute unit a kernel is built for (its register
-// budget): two for the eight-wave blocks of lanes owning up to 16 columns,
-// else one.  choose_rows may still place one of them per compute unit.
+// Row-pass blocks per compute unit: two for the eight-wave blocks of lanes
+// owning up to 16 columns, else one.
 constexpr int rows_blocks_per_cu(int NW, int G) { return (NW == 8 && G <= 16) ? 2 : 1; }
 
 inline int next_pow2(int v) {
