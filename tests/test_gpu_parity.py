@@ -151,10 +151,11 @@ def test_gate_logits_shapes(T, d, E):
     assert err.max() <= 1e-4, f"gate logits max error {err.max()}"
 
 
-def test_gate_full():
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_gate_full(seed):
     w = WORKLOADS["gate_top2"]
-    print("case gate_full", flush=True)
-    inp, p, g, r = _gate_case(w, 0)
+    print(f"case gate_full seed={seed}", flush=True)
+    inp, p, g, r = _gate_case(w, seed)
     # backward on the gate logits the forward wrote (the forward on them was
     # compared with the oracle in _gate_case)
     rr = oracle_forward(params_of(w, d=0), g["logits"])
