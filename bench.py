@@ -97,6 +97,15 @@ def alg_bytes(w, T):
             "route_backward": bwd, "gate_backward": gate_bwd, "forward": forward}
 
 
+def one_launch_path(w):
+    """Whether moe_route routes this workload in one launch: E of 1, 2, 4 or
+    8, k*E at most 16 and microbatches of at most 32768 logits, as the
+    library decides in moe_route."""
+    Tm = w.T // w.n_micro
+    return (w.E in (1, 2, 4, 8) and w.k * w.E <= 16 and Tm * w.E <= 32768
+            and w.n_micro <= 65535)
+
+
 def kernel_source_hash():
     """Hash of the HIP sources, to tell whether stored counters still apply."""
     import glob
@@ -423,6 +432,9 @@ def main():
         dom_name, dom_bytes, dom_ms = "gate+route forward (no per-kernel split)", ab["forward"], ms_step
     elif w.backward and bwd_ms > rows_ms:
         dom_name, dom_bytes, dom_ms = "route_backward_kernel", ab["route_backward"], bwd_ms
+    elif one_launch_path(w):
+        # one kernel does the whole forward: the row-pass events time it
+        dom_name, dom_bytes, dom_ms = "route_small_kernel", ab["forward"], rows_ms
     else:
         dom_name, dom_bytes, dom_ms = "route_rows_kernel", ab["rows"], rows_ms
     if gate_bwd:  # the kernel the gate backward launches for this E (its reduce step aside)

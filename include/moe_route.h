@@ -64,6 +64,11 @@ extern "C" {
 #define MOE_P_MASKED      16u /* P_e from each token's picks only, over Tm*k
                                  ([p1] 4.4's top-k code); default: the mean
                                  softmax over all tokens ([p1] 4.2)          */
+#define MOE_MULTI_KERNEL  32u /* route the small microbatches moe_route
+                                 takes in one launch (see there) with the
+                                 multi-kernel path, as larger ones
+                                 (integer outputs identical, floating-point
+                                 ones up to summation order; for comparison) */
 
 /* Bits of the optional status word (set for the whole call). */
 #define MOE_STATUS_NONFINITE 1 /* a row had a NaN/+inf logit, or only -inf;
@@ -115,8 +120,9 @@ typedef struct {
  *                          max f, min f ([p2] 4.2)
  *   status   [1] int32     nullable; MOE_STATUS_* bits of this call
  *   row_pass_events        nullable pair of hipEvent_t handles created by the
- *                          caller; when both are set the row-pass kernel is
- *                          launched with them as its start and stop events
+ *                          caller; when both are set the row-pass kernel (on
+ *                          the one-launch path, that kernel) is launched
+ *                          with them as its start and stop events
  *                          (hipExtLaunchKernel: the runtime stamps them from
  *                          that kernel's own dispatch, as a kernel trace
  *                          does; hipEventElapsedTime then gives its time)
@@ -173,7 +179,10 @@ int moe_route_capacity(const moe_route_params *p, int32_t *capacity);
  * steer the expert choice; here it enters the choice only -- experts are
  * ranked by the fp32 sum l + b_e (ties to the lower expert) while the gate
  * weights, P and the aux loss use the unbiased softmax.
- * Enqueues the whole forward on stream.  workspace: device buffer of at
+ * Enqueues the whole forward on stream: the gate GEMM (gate path), then one
+ * launch when E is 1, 2, 4 or 8, k*E <= 16 and a microbatch holds at most
+ * 32768 logits (unless MOE_MULTI_KERNEL), else a row pass, a block combine
+ * and the dispatch scatter.  workspace: device buffer of at
  * least moe_route_workspace_size() bytes, used only during the call's
  * kernels (calls sharing one workspace must be ordered on one stream).
  */

@@ -24,6 +24,7 @@ MOE_SAVE_ROW_STATS = 2
 MOE_WRITE_INV_PERM = 4
 MOE_SELECT_BIAS = 8
 MOE_P_MASKED = 16
+MOE_MULTI_KERNEL = 32
 
 MOE_STATUS_NONFINITE = 1
 MOE_STATUS_INTERNAL = 2
@@ -106,10 +107,10 @@ def load(path=None):
 
 def make_params(T, E, k, n_micro=1, d=0, capacity_factor=1.0, capacity=-1, alpha=0.01,
                 renorm=False, save_row_stats=False, inv_perm=False, select_bias=False,
-                p_masked=False):
+                p_masked=False, multi_kernel=False):
     flags = ((MOE_RENORM_TOPK if renorm else 0) | (MOE_SAVE_ROW_STATS if save_row_stats else 0)
              | (MOE_WRITE_INV_PERM if inv_perm else 0) | (MOE_SELECT_BIAS if select_bias else 0)
-             | (MOE_P_MASKED if p_masked else 0))
+             | (MOE_P_MASKED if p_masked else 0) | (MOE_MULTI_KERNEL if multi_kernel else 0))
     return moe_route_params(int(T), int(E), int(k), int(n_micro), int(d), int(capacity),
                             float(capacity_factor), float(alpha), flags)
 

@@ -2,7 +2,8 @@
 // validation on the host, workspace sizing, and the launch sequence
 //   [gate transpose + gate GEMM] -> row pass -> block scan + statistics
 //   -> dispatch scatter
-// for the forward, and the single streaming pass of the backward.
+// for the forward (one launch after the gate GEMM for small microbatches),
+// and the single streaming pass of the backward.
 #include <climits>
 #include <cmath>
 #include <mutex>
@@ -20,8 +21,8 @@ namespace {
 
 using moe::RowCfg;
 
-constexpr uint32_t kKnownFlags =
-    MOE_RENORM_TOPK | MOE_SAVE_ROW_STATS | MOE_WRITE_INV_PERM | MOE_SELECT_BIAS | MOE_P_MASKED;
+constexpr uint32_t kKnownFlags = MOE_RENORM_TOPK | MOE_SAVE_ROW_STATS | MOE_WRITE_INV_PERM |
+                                  MOE_SELECT_BIAS | MOE_P_MASKED | MOE_MULTI_KERNEL;
 constexpr size_t kMaxLds = 160 * 1024;
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
@@ -198,6 +199,32 @@ int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
     const bool timed = out->row_pass_events[0] && out->row_pass_events[1];
     const moe::LaunchEvents ev{static_cast<hipEvent_t>(out->row_pass_events[0]),
                                static_cast<hipEvent_t>(out->row_pass_events[1])};
+
+    moe::ScatterArgs ca{};
+    ca.n_micro = p->n_micro;
+    ca.alpha = p->alpha;
+    ca.p_masked = (p->flags & MOE_P_MASKED) ? 1 : 0;
+    ca.counts = out->counts; ca.offsets = out->offsets; ca.f = out->f; ca.P = out->P;
+    ca.aux = out->aux_loss; ca.cv = out->cv; ca.max_over_mean = out->max_over_mean;
+    ca.extra = out->extra_stats;
+    ca.T = p->T; ca.E = p->E; ca.k = p->k; ca.Tm = Tm;
+    ca.capacity = int(capacity_of(p));
+    ca.perm = out->perm;
+    ca.inv_perm = (p->flags & MOE_WRITE_INV_PERM) ? out->inv_perm : nullptr;
+    ca.dropped = out->dropped; ca.status = out->status;
+
+    if (!(p->flags & MOE_MULTI_KERNEL) && moe::small_path_fits(Tm, p->E, p->k, p->n_micro)) {
+        // small microbatches: the whole forward in one launch
+        moe::SmallArgs sm{};
+        sm.logits = L;
+        sm.bias = ra.bias;
+        sm.nb = moe::small_row_blocks(Tm);
+        sm.renorm = ra.renorm; sm.save_stats = ra.save_stats;
+        sm.topk_idx = out->topk_idx; sm.topk_w = out->topk_w; sm.row_stats = out->row_stats;
+        sm.out = ca;
+        if (moe::launch_route_small(sm, st, timed ? &ev : nullptr) != hipSuccess) return MOE_ERR_HIP;
+        return MOE_OK;
+    }
     if (moe::launch_route_rows(c, ra, st, timed ? &ev : nullptr) != hipSuccess) return MOE_ERR_HIP;
 
     moe::ScanArgs sa{};
@@ -211,7 +238,6 @@ int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
     const int fold_q = moe::scatter_fold_groups(p->E, p->k, c.bpm, scat_nw);
     if (fold_q == 0 && moe::launch_route_scan(c, sa, st) != hipSuccess) return MOE_ERR_HIP;
 
-    moe::ScatterArgs ca{};
     ca.topk_idx = out->topk_idx; ca.colprefix = ws.colprefix; ca.split_tot = ws.split_tot;
     ca.split_P = ws.split_P;
     ca.cnt_part = ws.cnt_part; ca.P_part = ws.P_part; ca.flag_part = ws.flag_part;
@@ -219,19 +245,9 @@ int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
     // few row blocks: the statistics get workgroups of their own, so that no
     // block adds them to its share of the permutation
     ca.stats_sep = (c.B + p->n_micro <= moe::kAssumedCUs) ? 1 : 0;
-    ca.n_micro = p->n_micro;
-    ca.alpha = p->alpha;
-    ca.p_masked = (p->flags & MOE_P_MASKED) ? 1 : 0;
-    ca.counts = out->counts; ca.offsets = out->offsets; ca.f = out->f; ca.P = out->P;
-    ca.aux = out->aux_loss; ca.cv = out->cv; ca.max_over_mean = out->max_over_mean;
-    ca.extra = out->extra_stats;
-    ca.T = p->T; ca.E = p->E; ca.k = p->k; ca.Tm = Tm; ca.bpm = c.bpm; ca.nsplit = c.nsplit;
+    ca.bpm = c.bpm; ca.nsplit = c.nsplit;
     ca.rows_per_wave = moe::scatter_rows_per_wave(p->E, p->k, scat_nw);
-    ca.capacity = int(capacity_of(p));
     ca.vec_idx = (p->k % 4 == 0 && aligned(out->topk_idx, 16)) ? 1 : 0;
-    ca.perm = out->perm;
-    ca.inv_perm = (p->flags & MOE_WRITE_INV_PERM) ? out->inv_perm : nullptr;
-    ca.dropped = out->dropped; ca.status = out->status;
     if (moe::launch_route_scatter(c, ca, st) != hipSuccess) return MOE_ERR_HIP;
     return MOE_OK;
 }

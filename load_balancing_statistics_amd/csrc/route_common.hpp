@@ -7,6 +7,8 @@
 // S consecutive floats of one row and a wave reads 64/S rows at once.
 #pragma once
 
+#include <climits>
+
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -266,6 +268,25 @@ struct ScatterArgs {
     float* extra;
 };
 
+// One-launch path for small microbatches (route_small.hip): E a power of
+// two up to kSmallMaxE, k*E up to kSmallMaxPicks and at most kSmallMaxLogits
+// logits a microbatch, where every workgroup selects the whole microbatch
+// itself (its cost grows with k*E per row and with the microbatch).
+constexpr int kSmallMaxE = 8;
+constexpr int kSmallMaxPicks = 16;
+constexpr long kSmallMaxLogits = 32768;
+
+struct SmallArgs {
+    const float* logits;
+    const float* bias;  // [E] selection bias, or nullptr
+    int nb;             // row blocks per microbatch (small_row_blocks)
+    int renorm, save_stats;
+    int32_t* topk_idx;
+    float* topk_w;
+    float* row_stats;
+    ScatterArgs out;    // sizes, capacity, alpha, permutation and statistics outputs
+};
+
 struct BackArgs {
     const float* logits;
     const float* row_stats;
@@ -359,6 +380,9 @@ int scatter_rows_per_wave(int E, int k, int NW);
 size_t scatter_lds_bytes(int E, int k, int NW);
 int scatter_fold_groups(int E, int k, int bpm, int NW);
 hipError_t launch_route_backward(const RowCfg& c, const BackArgs& a, hipStream_t st);
+bool small_path_fits(int Tm, int E, int k, int n_micro);
+int small_row_blocks(int Tm);
+hipError_t launch_route_small(const SmallArgs& a, hipStream_t st, const LaunchEvents* ev);
 hipError_t launch_bias_update(const BiasArgs& a, hipStream_t st);
 hipError_t launch_gate_backward(const GateBackArgs& a, hipStream_t st);
 hipError_t launch_eplb(const EplbArgs& a, hipStream_t st);
@@ -620,6 +644,95 @@ template <class T>
 MOE_DEV T load_or(const T* p, long i, bool ok, T dflt) {
     const T v = p[ok ? i : 0];
     return ok ? v : dflt;
+}
+
+// Counts, offsets and balance statistics of microbatch mb, by one block of
+// NW waves, from the counts tot[0..E) and their exclusive prefix lofs[0..E]
+// (both in LDS), in fp64 with every sum in a fixed order:
+//   f_e = counts_e/(Tm*k) and P_e = probability sum/Tm (or /(Tm*k) for the
+//   masked form of mhpq.cn section 4.4, whose sums cover the picks only) with
+//   aux = alpha*E*sum_e f_e*P_e (mhpq.cn sections 4.2, 4.4; codechina.net
+//   article 413310 section 2.2), CV = population std/mean and balance degree
+//   1-(max-mean)/mean (page cnvsn.com/news/335486 sections 3.1, 5.1),
+//   max/mean load (mhpq.cn section 5.4), entropy and max/min share of f
+//   (codechina.net section 4.2), kept and dropped assignments under C.
+// Every thread forms the terms of its experts (psum[it]: the probability sum
+// of expert tid + it*NW*64 over the splits) into q, four arrays of E doubles
+// in LDS; then waves 0..5 each reduce one quantity (lane-strided sums in
+// expert order, then the lanes) and write its results.  q is free LDS
+// scratch of the caller; the function ends with a barrier.
+template <int NW, int EPT>
+__device__ void microbatch_statistics(const ScatterArgs& a, int mb, const int* tot, const int* lofs,
+                                      const double* psum, double* q) {
+    static_assert(NW >= 6, "one wave per reduced quantity");
+    const int E = a.E;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const double total = double(a.Tm) * double(a.k);
+    const double mean = total / double(E);
+    const long cb = long(mb) * E;
+    // f and P scale by reciprocals formed once (within an ulp of dividing)
+    const double inv_total = 1.0 / total;
+    const double inv_pden = a.p_masked ? inv_total : 1.0 / double(a.Tm);
+#pragma unroll
+    for (int it = 0; it < EPT; ++it) {
+        const int e = tid + it * NW * 64;
+        if (e >= E) break;
+        const int cnt = tot[e];
+        const double fe = double(cnt) * inv_total;
+        const double pe = psum[it] * inv_pden;
+        a.counts[cb + e] = cnt;
+        a.offsets[long(mb) * (E + 1) + e] = lofs[e];
+        if (a.f) a.f[cb + e] = float(fe);
+        if (a.P) a.P[cb + e] = float(pe);
+        q[e] = fe * pe;
+        q[E + e] = (double(cnt) - mean) * (double(cnt) - mean);
+        // -f ln f with a hardware fp32 log2 (about 1e-7 relative per term;
+        // the terms share one sign, so the sum keeps that precision)
+        q[2 * E + e] = fe > 0.0 ? -fe * (double(__builtin_amdgcn_logf(float(fe))) * 0.69314718055994531) : 0.0;
+        q[3 * E + e] = double((a.capacity >= 0 && cnt > a.capacity) ? a.capacity : cnt);
+    }
+    __syncthreads();
+    if (wave < 4) {
+        // sum of terms: f.P, squared deviations, entropy terms, kept
+        const double* v = q + wave * E;
+        double acc = 0.0;
+        for (int e = lane; e < E; e += 64) acc += v[e];
+        acc = wave_sum_f64(acc);
+        if (lane == 0) {
+            float* x = a.extra ? a.extra + long(mb) * 8 : nullptr;
+            if (wave == 0) {
+                a.aux[mb] = float(double(a.alpha) * double(E) * acc);
+                a.offsets[long(mb) * (E + 1) + E] = lofs[E];
+            } else if (wave == 1) {
+                a.cv[mb] = float(sqrt(acc / double(E)) / mean);
+            } else if (wave == 2) {
+                if (x) x[2] = float(acc);
+            } else if (x) {
+                x[3] = float(acc);
+                x[4] = float(total - acc);
+                x[5] = float(a.capacity);
+            }
+        }
+    } else if (wave < 6) {
+        // largest (wave 4) and smallest (wave 5) count
+        int m = (wave == 4) ? -1 : INT_MAX;
+        for (int e = lane; e < E; e += 64) m = (wave == 4) ? max(m, tot[e]) : min(m, tot[e]);
+        m = (wave == 4) ? wave_max_i(m) : wave_min_i(m);
+        if (lane == 0) {
+            float* x = a.extra ? a.extra + long(mb) * 8 : nullptr;
+            if (wave == 4) {
+                a.max_over_mean[mb] = float(double(m) / mean);
+                if (x) {
+                    x[1] = float(1.0 - (double(m) - mean) / mean);
+                    x[6] = float(double(m) / total);
+                }
+            } else if (x) {
+                x[0] = float(double(m) / mean);
+                x[7] = float(double(m) / total);
+            }
+        }
+    }
+    __syncthreads();
 }
 
 }  // namespace dev

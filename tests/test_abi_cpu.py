@@ -279,3 +279,27 @@ def test_sinkhorn_validation(lbs):
     assert lib.moe_sinkhorn_plan(8, *ok, 1.0, -1, *outs, None) == B.MOE_ERR_INVALID_ARG
     assert lib.moe_sinkhorn_plan(8, f, f, None, 1.0, 50, *outs, None) == B.MOE_ERR_INVALID_ARG
     assert lib.moe_sinkhorn_plan(8, f + 4, f, f, 1.0, 50, *outs, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_flag_values_match_header(lbs):
+    """Every MOE_* flag and status bit of the header has the binding's value;
+    an unknown flag bit is an invalid argument, the known ones are accepted."""
+    src = open(HEADER).read()
+    defs = dict(re.findall(r"#define\s+(MOE_\w+)\s+\(?(-?\d+)u?\)?", src))
+    B = lbs._binding
+    names = ["MOE_RENORM_TOPK", "MOE_SAVE_ROW_STATS", "MOE_WRITE_INV_PERM", "MOE_SELECT_BIAS",
+             "MOE_P_MASKED", "MOE_MULTI_KERNEL", "MOE_STATUS_NONFINITE", "MOE_STATUS_INTERNAL"]
+    for n in names:
+        assert int(defs[n]) == getattr(B, n), n
+    known = 0
+    for n in names[:6]:
+        known |= getattr(B, n)
+    p = lbs.make_params(4096, 8, 1, multi_kernel=True)
+    assert lbs.moe_route_workspace_size(p) > 0
+    for bit in range(32):
+        if known & (1 << bit):
+            continue
+        q = lbs.make_params(4096, 8, 1)
+        q.flags = 1 << bit
+        n = ctypes.c_size_t(0)
+        assert lbs.load().moe_route_workspace_size(ctypes.byref(q), ctypes.byref(n)) == B.MOE_ERR_INVALID_ARG, bit

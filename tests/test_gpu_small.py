@@ -1,8 +1,9 @@
-"""Small single-microbatch batches (E <= 16, T up to 8192: a few row blocks,
-the scatter folding the block combine in) against the oracle, element by
-element: sizes around the 64-row wave step and the 1024-row marks, expert
-counts off the vector width, every option, ties, drops and non-finite
-rows."""
+"""Small single-microbatch batches (E <= 16, T up to 8192) against the
+oracle, element by element, on both paths: the one launch (E of 1, 2, 4 or
+8 with k*E <= 16) and the multi-kernel path (a few row blocks, the scatter folding the
+block combine in; forced with MOE_MULTI_KERNEL): sizes around the 64-row
+wave step and the 1024-row marks, expert counts off the vector width, every
+option, ties, drops and non-finite rows."""
 import numpy as np
 import pytest
 
@@ -33,13 +34,13 @@ CASES = [
 ]
 
 
-def _run(T, E, k, cf, opts, seed, logits=None):
+def _run(T, E, k, cf, opts, seed, logits=None, multi=False):
     rng = np.random.default_rng(seed)
     L = rng.standard_normal((T, E), dtype=np.float32) if logits is None else logits
     sb = (0.5 * rng.standard_normal(E)).astype(np.float32) if "bias" in opts else None
     p = lbs.make_params(T, E, k, capacity_factor=cf, alpha=0.01, renorm="renorm" in opts,
                         save_row_stats=True, inv_perm=True, select_bias=sb is not None,
-                        p_masked="masked" in opts)
+                        p_masked="masked" in opts, multi_kernel=multi)
     inputs = {"logits": L}
     if sb is not None:
         inputs["select_bias"] = sb
@@ -49,21 +50,23 @@ def _run(T, E, k, cf, opts, seed, logits=None):
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"T{c[0]}_E{c[1]}_k{c[2]}_cf{c[3]}_{c[4] or 'plain'}" for c in CASES])
-def test_small_forward(case):
+@pytest.mark.parametrize("multi", [False, True], ids=["default", "multi_kernel"])
+def test_small_forward(case, multi):
     T, E, k, cf, opts = case
-    print(f"case small T={T} E={E} k={k} cf={cf} {opts}", flush=True)
+    print(f"case small T={T} E={E} k={k} cf={cf} {opts} multi={multi}", flush=True)
     for seed in (0, 1):
-        p, g, r = _run(T, E, k, cf, opts, seed)
+        p, g, r = _run(T, E, k, cf, opts, seed, multi=multi)
         compare_forward(g, r, p)
 
 
-def test_small_ties():
+@pytest.mark.parametrize("multi", [False, True], ids=["default", "multi_kernel"])
+def test_small_ties(multi):
     """Integer logits: most rows hold ties, broken toward the lower expert."""
     T, E, k = 4000, 8, 3
-    print(f"case small ties T={T} E={E} k={k}", flush=True)
+    print(f"case small ties T={T} E={E} k={k} multi={multi}", flush=True)
     rng = np.random.default_rng(7)
     L = rng.integers(-2, 3, size=(T, E)).astype(np.float32)
-    p, g, r = _run(T, E, k, 1.0, "renorm", 7, logits=L)
+    p, g, r = _run(T, E, k, 1.0, "renorm", 7, logits=L, multi=multi)
     compare_forward(g, r, p)
 
 
