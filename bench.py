@@ -441,6 +441,8 @@ def main():
         traffic = measured_traffic(w.name, "moe::gate_backward_bf16_kernel" if w.E <= 8
                                    else "moe::gate_backward_mfma_kernel" if w.E <= 16
                                    else "moe::gate_backward_kernel<")
+    elif one_launch_path(w):
+        traffic = measured_traffic(w.name, "moe::route_small_kernel")
     else:
         traffic = measured_traffic(w.name, dom_name) if w.d == 0 else None
     achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
