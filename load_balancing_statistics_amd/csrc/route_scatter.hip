@@ -41,7 +41,7 @@ using namespace dev;
 constexpr int kScatMaxWaves = 16;
 constexpr int kSplitBatch = 8;
 constexpr int kFoldLoads = 16;  // row blocks a thread sums when the scatter folds the combine in
-constexpr int kFoldGroups = 2;  // at most this many row-block groups per expert
+constexpr int kFoldGroups = 16;  // at most this many row-block groups per expert
 
 // Exclusive scan of n LDS ints v[0..n) into out[0..n] (out[n] = total).
 __device__ void block_excl_scan(const int* v, int n, int* out, int* wsum) {
@@ -360,9 +360,12 @@ size_t lds_for(int E, int NW, int rpw, int k) {
 // groups that a thread sums at most kFoldLoads row blocks, when that takes at
 // most kFoldGroups groups, the groups of every expert fit the block's
 // threads and their sums (16 bytes each) the LDS free before the first
-// window; 0 otherwise (the combine kernel runs).  Measured: folding saves
-// 2-3 us a call with one or two groups; with 16 (65536 tokens over 256 row
-// blocks, E=64) the combine in LDS cost what the kernel launch saved.
+// window; 0 otherwise (the combine kernel runs).  Measured per call: 16384
+// tokens, E=8 top-2 (4 groups) 14.3 -> 11.9 us; 131072 tokens, E=8 top-1 (16
+// groups) 15.6 -> 13.9 us; 32768 tokens, E=32 top-2 (6 groups) 21.1 ->
+// 18.3 us.  With more (group, expert) pairs than threads (65536 tokens, E=64:
+// 1024 pairs, two rounds of loads) it was 19.7 against 19.2 us, so such
+// shapes keep the combine kernel.
 int scatter_fold_groups(int E, int k, int bpm, int NW) {
     const long Q = (bpm + kFoldLoads - 1) / kFoldLoads;
     const size_t room = size_t(NW) * E * 12 + size_t(NW) * scatter_rows_per_wave(E, k, NW) * k * 8;

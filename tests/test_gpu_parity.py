@@ -196,11 +196,16 @@ EDGE = [
     (2500, 20, 1, 1, 1.05, -1, False, "normal"),
     (2048, 24, 1, 1, 1.0, -1, False, "quantized"),
     (1000, 13, 2, 1, 1.3, -1, True, "normal"),
-    # few row blocks in all: the statistics in workgroups of their own, with
-    # the split combine kernel (64 row blocks a microbatch) and without it
+    # few row blocks in all: the statistics in workgroups of their own, the
+    # scatter summing 64 row blocks a microbatch (four groups) or 32 (two)
     (32768, 8, 2, 2, 1.25, -1, True, "normal"),
     (16384, 16, 4, 4, 1.0, -1, True, "quantized"),
     (6000, 64, 2, 3, 1.1, -1, False, "normal"),
+    # the scatter folding in up to 16 groups of row blocks (no combine kernel)
+    (131072, 8, 1, 1, 1.25, -1, False, "normal"),    # 256 row blocks, 16 groups
+    (65536, 16, 4, 1, 1.0, -1, True, "quantized"),   # 16 groups, ties
+    (32768, 32, 2, 1, 1.1, -1, True, "normal"),      # 6 groups
+    (49152, 8, 2, 3, 1.0, 50, True, "normal"),       # three microbatches, explicit capacity
 ]
 
 
