@@ -2,9 +2,9 @@
 //
 // A microbatch of at most kSmallMaxLogits logits over a power-of-two number
 // of experts up to 8, with k*E at most 16 (Switch top-1 over 4096 tokens and
-// 8 experts is one), costs the
-// multi-kernel path its launches and their first memory round trips, not its
-// bytes -- the launch-count lesson of the LoongForge TAOT blog, section 3.
+// 8 experts is one), costs the multi-kernel path its launches and their
+// first memory round trips, not its bytes -- the launch-count lesson of the
+// LoongForge TAOT blog, section 3.
 // Here no workgroup waits for another: every workgroup of a microbatch reads
 // all of it (at most 128 KB, from L2 after the first) and selects every
 // token's experts itself, which gives it the counts before its own rows and
@@ -273,6 +273,11 @@ route_small_kernel(const SmallArgs a)
     row_softmax<NE>(xo, m, ssum, ex);
     int pc[NE];
     float pw[NE];
+#pragma unroll
+    for (int j = 0; j < NE; ++j) {
+        pc[j] = 0;
+        pw[j] = 0.f;
+    }
     uint32_t pm;
     uint64_t jp;
     select_row<NE, BIAS>(xo, bl, k, pm, jp, [&](int j, int col) {
@@ -285,7 +290,7 @@ route_small_kernel(const SmallArgs a)
     if (!own) pm = 0;
     float esum = 0.f;
 #pragma unroll
-    for (int j = 0; j < NE; ++j) esum += (j < k) ? pw[j] : 0.f;
+    for (int j = 0; j < NE; ++j) esum += pw[j];  // (slots past k hold 0)
     const float rden = a.renorm ? __builtin_amdgcn_rcpf(esum) : __builtin_amdgcn_rcpf(ssum);
     if (own) {
 #pragma unroll
