@@ -257,7 +257,8 @@ struct ScatterArgs {
     int32_t* inv_perm;
     uint8_t* dropped;
     int32_t* status;
-    // per-microbatch results, written by the first block of each microbatch
+    // per-microbatch results, written by the microbatch's statistics
+    // workgroup or shared by its first six blocks
     int32_t* counts;
     int32_t* offsets;
     float* f;
@@ -661,9 +662,14 @@ MOE_DEV T load_or(const T* p, long i, bool ok, T dflt) {
 // in LDS; then waves 0..5 each reduce one quantity (lane-strided sums in
 // expert order, then the lanes) and write its results.  q is free LDS
 // scratch of the caller; the function ends with a barrier.
+// parts selects what this block forms, so that several blocks can share
+// the work: bit 0 the per-expert outputs (counts, offsets, f, P) and the aux
+// loss -- the only part that reads psum --, bit w (w = 1..5) the quantity
+// wave w reduces; kStatsAll is everything.
+constexpr int kStatsAll = 0x3F;
 template <int NW, int EPT>
 __device__ void microbatch_statistics(const ScatterArgs& a, int mb, const int* tot, const int* lofs,
-                                      const double* psum, double* q) {
+                                      const double* psum, double* q, int parts = kStatsAll) {
     static_assert(NW >= 6, "one wave per reduced quantity");
     const int E = a.E;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -679,20 +685,25 @@ __device__ void microbatch_statistics(const ScatterArgs& a, int mb, const int* t
         if (e >= E) break;
         const int cnt = tot[e];
         const double fe = double(cnt) * inv_total;
-        const double pe = psum[it] * inv_pden;
-        a.counts[cb + e] = cnt;
-        a.offsets[long(mb) * (E + 1) + e] = lofs[e];
-        if (a.f) a.f[cb + e] = float(fe);
-        if (a.P) a.P[cb + e] = float(pe);
-        q[e] = fe * pe;
-        q[E + e] = (double(cnt) - mean) * (double(cnt) - mean);
+        if (parts & 1) {
+            const double pe = psum[it] * inv_pden;
+            a.counts[cb + e] = cnt;
+            a.offsets[long(mb) * (E + 1) + e] = lofs[e];
+            if (a.f) a.f[cb + e] = float(fe);
+            if (a.P) a.P[cb + e] = float(pe);
+            q[e] = fe * pe;
+        }
+        if (parts & 2) q[E + e] = (double(cnt) - mean) * (double(cnt) - mean);
         // -f ln f with a hardware fp32 log2 (about 1e-7 relative per term;
         // the terms share one sign, so the sum keeps that precision)
-        q[2 * E + e] = fe > 0.0 ? -fe * (double(__builtin_amdgcn_logf(float(fe))) * 0.69314718055994531) : 0.0;
-        q[3 * E + e] = double((a.capacity >= 0 && cnt > a.capacity) ? a.capacity : cnt);
+        if (parts & 4)
+            q[2 * E + e] = fe > 0.0 ? -fe * (double(__builtin_amdgcn_logf(float(fe))) * 0.69314718055994531) : 0.0;
+        if (parts & 8) q[3 * E + e] = double((a.capacity >= 0 && cnt > a.capacity) ? a.capacity : cnt);
     }
     __syncthreads();
-    if (wave < 4) {
+    if (wave < 6 && !((parts >> wave) & 1)) {
+        // not this block's quantity
+    } else if (wave < 4) {
         // sum of terms: f.P, squared deviations, entropy terms, kept
         const double* v = q + wave * E;
         double acc = 0.0;

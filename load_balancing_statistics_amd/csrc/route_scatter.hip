@@ -10,10 +10,11 @@
 //   earlier blocks of its split),
 // offsets being the exclusive prefix sum, in expert order, of the
 // microbatch's counts (the sums of its split counts), which every block
-// forms for itself.  The first block of each microbatch also writes the
-// counts, the offsets and the balance statistics -- or, when the row blocks
-// and one more workgroup per microbatch fit the chip at once, that extra
-// workgroup does, so that no block adds them to its share of the rows.
+// forms for itself.  The first six blocks of each microbatch also share
+// the counts, the offsets and the balance statistics, one reduced quantity
+// each -- or, when the row blocks and one more workgroup per microbatch can
+// run at once, that extra workgroup forms them all, so that no block adds
+// them to its share of the rows.
 //
 // A token picks an expert at most once (its top-k are distinct), so inside an
 // expert the (t, j) order is the token order.  The block walks its rows in
@@ -157,7 +158,15 @@ route_scatter_kernel(const ScatterArgs a)
     // to the expert's offset base[e] (the count in the microbatch's earlier
     // row blocks) and, for the statistics, the probability sum psum
     constexpr int EPT = (MOE_ROUTE_MAX_E + NW * 64 - 1) / (NW * 64);  // experts per thread
-    const bool stats_block = a.stats_sep ? stats_only : bi == 0;
+    // the statistics: all of them in the statistics workgroup, else spread
+    // over the microbatch's first six row blocks (one reduced quantity
+    // each; block 0 also the per-expert outputs and the aux loss), so no
+    // block adds more than a sixth of them to its rows
+    const int parts = a.stats_sep ? (stats_only ? kStatsAll : 0)
+                    : a.bpm >= 6  ? (bi < 6 ? (1 << bi) : 0)
+                                  : (bi == 0 ? kStatsAll : 0);
+    const bool stats_block = parts != 0;
+    const bool need_p = (parts & 1) != 0;  // only part 0 reads the probability sums
     double psum[EPT];
 #pragma unroll
     for (int it = 0; it < EPT; ++it) psum[it] = 0.0;
@@ -241,7 +250,7 @@ route_scatter_kernel(const ScatterArgs a)
 #pragma unroll
                 for (int v = 0; v < kSplitBatch; ++v)
                     sv[v] = load_or(a.split_tot, sb + long(sp0 + v) * E, sp0 + v < a.nsplit, 0);
-                if (stats_block) {
+                if (need_p) {
 #pragma unroll
                     for (int v = 0; v < kSplitBatch; ++v)
                         pv[v] = load_or(a.split_P, sb + long(sp0 + v) * E, sp0 + v < a.nsplit, 0.0);
@@ -251,7 +260,7 @@ route_scatter_kernel(const ScatterArgs a)
                     t += sv[v];
                     pre += (sp0 + v < my_split) ? sv[v] : 0;
                 }
-                if (stats_block) {
+                if (need_p) {
 #pragma unroll
                     for (int v = 0; v < kSplitBatch; ++v) psum[it] += pv[v];
                 }
@@ -271,7 +280,7 @@ route_scatter_kernel(const ScatterArgs a)
     }
     // tot and lofs are reused by the windows only after their first
     // barrier; the row masks' LDS is free until the first window
-    if (stats_block) microbatch_statistics<NW, EPT>(a, mb, tot, lofs, psum, reinterpret_cast<double*>(gm));
+    if (stats_block) microbatch_statistics<NW, EPT>(a, mb, tot, lofs, psum, reinterpret_cast<double*>(gm), parts);
     if (stats_only) return;
 
     uint64_t* mym = gm + wave * E;
