@@ -159,3 +159,39 @@ def test_one_launch_gate():
     assert_equal(one["logits"], multi["logits"], "logits")
     _compare_paths(one, multi)
     compare_forward(one, oracle_forward(params_of(w, d=0), one["logits"]), p)
+
+
+def _sweep(n=30, seed=77):
+    """Shapes and options drawn once inside the one-launch limits: E of 1, 2,
+    4 or 8, k*E <= 16, up to 32768 logits a microbatch, 1-5 microbatches."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        E = int(rng.choice([1, 2, 4, 8]))
+        k = int(rng.integers(1, min(E, 16 // E) + 1))
+        m = int(rng.choice([1, 1, 2, 3, 5]))
+        Tm = int(rng.integers(1, 32768 // E + 1))
+        cf = float(rng.choice([0.0, 0.5, 1.0, 1.1, 1.25]))
+        flags = dict(renorm=bool(rng.integers(0, 2)), p_masked=bool(rng.integers(0, 2)),
+                     select_bias=bool(rng.integers(0, 4) == 0))
+        out.append((Tm * m, E, k, m, cf, flags))
+    return out
+
+
+@pytest.mark.parametrize("case", _sweep(), ids=[f"T{c[0]}_E{c[1]}_k{c[2]}_m{c[3]}_cf{c[4]}" for c in _sweep()])
+def test_one_launch_sweep(case):
+    T, E, k, m, cf, flags = case
+    print(f"case one_launch sweep {case}", flush=True)
+    rng = np.random.default_rng(T * 13 + E * 7 + k)
+    L = (rng.standard_normal((T, E)) + rng.normal(0.0, 0.7, E)).astype(np.float32)
+    b = (0.5 * rng.standard_normal(E)).astype(np.float32) if flags["select_bias"] else None
+    mk = lambda **o: lbs.make_params(T, E, k, n_micro=m, capacity_factor=cf, alpha=0.01, save_row_stats=True,
+                                     inv_perm=True, **flags, **o)
+    inputs = {"logits": L}
+    if b is not None:
+        inputs["select_bias"] = b
+    p = mk()
+    one = gpu_forward(p, inputs)
+    multi = gpu_forward(mk(multi_kernel=True), inputs)
+    compare_forward(one, oracle_forward(p, L, select_bias=b), p)
+    _compare_paths(one, multi)
