@@ -206,6 +206,11 @@ EDGE = [
     (65536, 16, 4, 1, 1.0, -1, True, "quantized"),   # 16 groups, ties
     (32768, 32, 2, 1, 1.1, -1, True, "normal"),      # 6 groups
     (49152, 8, 2, 3, 1.0, 50, True, "normal"),       # three microbatches, explicit capacity
+    # grids too large for statistics workgroups: the statistics spread over a
+    # microbatch's first six row blocks (13 a microbatch), or all in block 0
+    # (3 a microbatch)
+    (81920, 256, 8, 40, 1.25, -1, True, "normal"),
+    (102400, 256, 8, 200, 1.0, -1, True, "quantized"),
 ]
 
 
