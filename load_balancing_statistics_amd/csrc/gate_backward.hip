@@ -407,8 +407,14 @@ gate_backward_bf16_kernel(const GateBackArgs a)
     const int cb = blockIdx.x * kB8Cols;  // the block's first column
     const int colx = cb + 8 * n;          // the lane's 8 columns of an X row
     const bool col_ok = colx < d;         // d % 8 == 0: all 8 in or all out
-    const long t0 = (long(blockIdx.y) * a.T) / gridDim.y;
-    const long t1 = (long(blockIdx.y + 1) * a.T) / gridDim.y;
+    // Row slices from the last: the forward's gate GEMM read X from the first
+    // row to the last, so its last rows are the likeliest still to be in the
+    // Infinity Cache, and walking the slices backwards meets them first
+    // (gate workload: 66.5 -> 65.5 us a call).  Slice sy keeps its own dWg
+    // partial, so the sums do not change.
+    const int sy = gridDim.y - 1 - blockIdx.y;
+    const long t0 = (long(sy) * a.T) / gridDim.y;
+    const long t1 = (long(sy + 1) * a.T) / gridDim.y;
     unsigned char* stage = lds + wave * kB8Stage;
     float* dlt = dlt_all[wave];  // dlogits of the wave's 32 rows: [k][e], pitch kDlPitch
 
@@ -574,7 +580,7 @@ gate_backward_bf16_kernel(const GateBackArgs a)
         }
         __syncthreads();
     }
-    float* part = a.dWg_part + long(blockIdx.y) * d * E;
+    float* part = a.dWg_part + long(sy) * d * E;
     for (int i = threadIdx.x; i < kB8Cols * E; i += kB8Waves * 64) {
         const int cc = i / E, e = i - (i / E) * E;
         const int col = cb + cc;
