@@ -634,8 +634,16 @@ route_backward_kernel(const BackArgs a)
         __syncthreads();
     }
 
+    // The block's rows from the last: the forward's row pass walked the same
+    // rows upwards, so the ones it read last -- the likeliest still to be in
+    // the Infinity Cache -- come first (v4 shape: 165.7 -> 164.9 us).  Every
+    // row's gradient stands alone, so the order changes no result.
     const long per_iter = long(NW) * W;
-    for (long row = row_begin + long(wave) * W + seg; row - seg < row_end; row += per_iter) {
+    const long n_it = (row_end - row_begin + per_iter - 1) / per_iter;
+    for (long it = n_it - 1; it >= 0; --it) {
+        const long base = row_begin + it * per_iter + long(wave) * W;  // wave-uniform
+        if (base >= row_end) continue;
+        const long row = base + seg;
         const bool valid = row < row_end;
         const long lr = valid ? row : row_end - 1;
         float x[G];
