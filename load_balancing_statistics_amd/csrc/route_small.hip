@@ -66,9 +66,10 @@ MOE_DEV uint32_t order_key(float v) {
     return o > 1u ? o : 1u;
 }
 
-// The k picks of a row, best first: k rounds of arg-max over the order keys,
-// scanning the experts in ascending order with a strict comparison, so ties
-// go to the lower expert; a picked column's key becomes 0.  pm gets bit e
+// The k picks of a row, best first: for k = 1 and 2 one scan over the
+// values, else k rounds of arg-max over the order keys; every scan goes
+// through the experts in ascending order with strict comparisons, so ties go
+// to the lower expert, and a picked column's key becomes 0.  pm gets bit e
 // for every picked expert and jp the pick index j of expert e in bits
 // [4e, 4e+4); pick(j, col) is called in order.
 template <int NE, bool BIAS, class Pick>
@@ -88,6 +89,31 @@ MOE_DEV void select_row(const float (&x)[NE], const float* bl, int k, uint32_t& 
         pm = 1u << col;
         jp = 0;
         pick(0, col);
+        return;
+    }
+    if (NE >= 2 && k == 2) {
+        // two picks in one scan: the best two values, the lower expert first
+        // among equals; the first two columns seed them, so both picks are
+        // always distinct experts (also for NaN values)
+        const float v0 = BIAS ? x[0] + bl[0] : x[0];
+        const float v1 = BIAS ? x[NE > 1 ? 1 : 0] + bl[NE > 1 ? 1 : 0] : x[NE > 1 ? 1 : 0];
+        const bool sw = v1 > v0;
+        float b1 = sw ? v1 : v0, b2 = sw ? v0 : v1;
+        int c1 = sw ? 1 : 0, c2 = sw ? 0 : 1;
+#pragma unroll
+        for (int e = 2; e < NE; ++e) {
+            const float v = BIAS ? x[e] + bl[e] : x[e];
+            const bool g1 = v > b1;
+            const bool g2 = !g1 && v > b2;
+            b2 = g1 ? b1 : (g2 ? v : b2);
+            c2 = g1 ? c1 : (g2 ? e : c2);
+            b1 = g1 ? v : b1;
+            c1 = g1 ? e : c1;
+        }
+        pm = (1u << c1) | (1u << c2);
+        jp = uint64_t(1) << (4 * c2);
+        pick(0, c1);
+        pick(1, c2);
         return;
     }
     uint32_t key[NE];
