@@ -180,9 +180,10 @@ int moe_route_capacity(const moe_route_params *p, int32_t *capacity);
  * ranked by the fp32 sum l + b_e (ties to the lower expert) while the gate
  * weights, P and the aux loss use the unbiased softmax.
  * Enqueues the whole forward on stream: the gate GEMM (gate path), then one
- * launch when E is 1, 2, 4 or 8, k*E <= 16 and a microbatch holds at most
- * 32768 logits (unless MOE_MULTI_KERNEL), else a row pass, a block combine
- * and the dispatch scatter.  workspace: device buffer of at
+ * launch when E is 1, 2, 4 or 8, k*E <= 16, a microbatch holds at most
+ * 32768 logits and there are at most 65535 microbatches (unless
+ * MOE_MULTI_KERNEL), else a row pass, a block combine (skipped when the
+ * scatter can sum the row blocks' partials itself) and the dispatch scatter.  workspace: device buffer of at
  * least moe_route_workspace_size() bytes, used only during the call's
  * kernels (calls sharing one workspace must be ordered on one stream).
  */
