@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="v3_shape")
+    ap.add_argument("--two-stream", action="store_true",
+                    help="also time two streams taking alternate batches (forward-only workloads; "
+                         "reported as detail.two_stream_ms_per_batch, never as value)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU work budget of the oracle baseline (0 disables it)")
     return ap.parse_args()
@@ -361,10 +364,12 @@ def main():
     def step(i, timed):
         src = srcs[i % ncopy]
         kw = dict(X=src, Wg=Wg) if w.d > 0 else dict(logits=src)
-        lbs.moe_route(p, out, ws, stream=stream, row_pass_events=ev_rows[i] if timed else None,
-                      select_bias=sbias, **kw)
         if w.bias_gamma > 0:  # one loss-free balancing step: the bias follows the loads
-            lbs.moe_route_bias_update(p, out["counts"], w.bias_gamma, sbias, stream=stream)
+            lbs.moe_route_with_bias_update(p, out, ws, sbias, w.bias_gamma, stream=stream,
+                                           row_pass_events=ev_rows[i] if timed else None, **kw)
+        else:
+            lbs.moe_route(p, out, ws, stream=stream, row_pass_events=ev_rows[i] if timed else None,
+                          select_bias=sbias, **kw)
         if w.backward:
             L = out["logits"] if w.d > 0 else src
             if timed:
@@ -410,11 +415,12 @@ def main():
     gb_ms = sum(hev.elapsed_ms(a, b) for a, b in ev_gb) / K if gate_bwd else None
     status = int(out["status"].item())
 
-    # 3) forward-only workloads: two streams taking alternate batches (each
-    # with its own outputs and workspace), as a caller routing a stream of
-    # batches can run them; reported beside the one-stream step, never as it
+    # 3) on request, forward-only workloads: two streams taking alternate
+    # batches (each with its own outputs and workspace), as a caller routing a
+    # stream of batches can run them; reported beside the one-stream step,
+    # never as it (off by default, so that a profiled run times one stream)
     two_stream_ms = None
-    if w.d == 0 and not w.backward and w.bias_gamma == 0:
+    if args.two_stream and w.d == 0 and not w.backward and w.bias_gamma == 0:
         s2 = torch.cuda.Stream()
         out2 = lbs.alloc_outputs(p, device=dev)
         ws2 = lbs.alloc_workspace(p, device=dev)

@@ -228,6 +228,21 @@ int moe_route_bias_update(const moe_route_params *p, const int32_t *counts, floa
                           float *bias, void *stream);
 
 /*
+ * One loss-free balancing step ([p1] 4.3) in one call: moe_route with the
+ * selection bias (p->flags must include MOE_SELECT_BIAS), then the bias step
+ * of moe_route_bias_update from this call's counts, applied to select_bias in
+ * place (read by the routing first, written after it).  The same results as
+ * the two calls in sequence; with one microbatch on the multi-kernel path the
+ * step is taken inside the dispatch scatter, which saves a launch.  gamma
+ * must be finite and >= 0.  Other arguments, workspace and return codes as
+ * for moe_route.
+ */
+int moe_route_with_bias_update(const moe_route_params *p, const float *logits, const uint16_t *X,
+                               const uint16_t *Wg, float *select_bias, float gamma,
+                               const moe_route_out *out, void *workspace, size_t workspace_bytes,
+                               void *stream);
+
+/*
  * Gradient with respect to the logits of
  *   L = sum_mb g_mb * aux_mb + sum_{t,j} d_topk_w[t,j] * topk_w[t,j]
  * with the forward's selection and counts held fixed ([p1] 4.2, [p2] 2.2:

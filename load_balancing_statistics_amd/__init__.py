@@ -11,5 +11,5 @@ from ._binding import (  # noqa: F401
     MOE_MULTI_KERNEL, MOE_P_MASKED, MOE_SELECT_BIAS, MOE_STATUS_INTERNAL, MOE_STATUS_NONFINITE, MOE_WRITE_INV_PERM, MoeRouteError,
     alloc_outputs, alloc_workspace, load, make_params, moe_eplb_plan, moe_gate_backward,
     moe_gate_backward_workspace_size, moe_route, moe_route_backward, moe_route_noalloc,
-    moe_route_bias_update, moe_route_capacity, moe_route_params, moe_route_strerror, moe_route_workspace_size,
+    moe_route_bias_update, moe_route_capacity, moe_route_with_bias_update, moe_route_params, moe_route_strerror, moe_route_workspace_size,
     moe_sinkhorn_plan)

@@ -88,6 +88,9 @@ def load(path=None):
     lib.moe_route_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.moe_route_backward.restype = ctypes.c_int
     lib.moe_route_bias_update.argtypes = [P, vp, ctypes.c_float, vp, vp]
+    lib.moe_route_with_bias_update.argtypes = [P, vp, vp, vp, vp, ctypes.c_float,
+                                               ctypes.POINTER(moe_route_out), vp, ctypes.c_size_t, vp]
+    lib.moe_route_with_bias_update.restype = ctypes.c_int
     lib.moe_route_bias_update.restype = ctypes.c_int
     lib.moe_gate_backward_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
     lib.moe_gate_backward_workspace_size.restype = ctypes.c_int
@@ -165,6 +168,23 @@ def moe_route(params, out, workspace, logits=None, X=None, Wg=None, stream=None,
                           if workspace is not None else 0, _stream(stream))
     if rc != MOE_OK:
         raise MoeRouteError(rc, "moe_route")
+
+
+def moe_route_with_bias_update(params, out, workspace, select_bias, gamma, logits=None, X=None, Wg=None,
+                               stream=None, row_pass_events=None):
+    """One loss-free balancing step: ``moe_route`` with ``select_bias`` (the
+    params must carry MOE_SELECT_BIAS), then ``select_bias`` stepped in place
+    by ``gamma`` from this call's counts."""
+    o = moe_route_out(*[None if out.get(n) is None else out[n].data_ptr() for n in _OUT_FIELDS])
+    if row_pass_events is not None:
+        o.row_pass_events[0] = row_pass_events[0]
+        o.row_pass_events[1] = row_pass_events[1]
+    rc = load().moe_route_with_bias_update(ctypes.byref(params), _ptr(logits), _ptr(X), _ptr(Wg),
+                                           _ptr(select_bias), float(gamma), ctypes.byref(o), _ptr(workspace),
+                                           workspace.numel() * workspace.element_size()
+                                           if workspace is not None else 0, _stream(stream))
+    if rc != MOE_OK:
+        raise MoeRouteError(rc, "moe_route_with_bias_update")
 
 
 def moe_route_noalloc(params, out, logits=None, X=None, Wg=None, stream=None, select_bias=None):

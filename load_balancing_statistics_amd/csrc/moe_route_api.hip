@@ -94,6 +94,12 @@ int scratch_of_current_device(void** out) {
     return MOE_OK;
 }
 
+// One selection-bias step from counts [m,E] (the rule of moe_route_bias_update).
+int bias_step(const moe_route_params* p, const int32_t* counts, float gamma, float* bias, hipStream_t st) {
+    moe::BiasArgs b{counts, bias, p->E, p->n_micro, int64_t(p->T) * p->k, gamma};
+    return moe::launch_bias_update(b, st) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 }  // namespace
 
 namespace moe {
@@ -144,9 +150,16 @@ int moe_route_capacity(const moe_route_params* p, int32_t* capacity) {
     return MOE_OK;
 }
 
-int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
-              const uint16_t* Wg, const float* select_bias, const moe_route_out* out,
-              void* workspace, size_t workspace_bytes_given, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward; with upd_bias, one selection-bias step from the call's counts
+// follows (inside the scatter for one microbatch on the multi-kernel path,
+// else by the update kernel after the forward).
+int route_impl(const moe_route_params* p, const float* logits, const uint16_t* X, const uint16_t* Wg,
+               const float* select_bias, const moe_route_out* out, void* workspace,
+               size_t workspace_bytes_given, void* stream, float* upd_bias, float upd_gamma) {
     int rc = check_shape(p);
     if (rc != MOE_OK) return rc;
     if (!out) return MOE_ERR_INVALID_ARG;
@@ -223,7 +236,7 @@ int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
         sm.topk_idx = out->topk_idx; sm.topk_w = out->topk_w; sm.row_stats = out->row_stats;
         sm.out = ca;
         if (moe::launch_route_small(sm, st, timed ? &ev : nullptr) != hipSuccess) return MOE_ERR_HIP;
-        return MOE_OK;
+        return upd_bias ? bias_step(p, out->counts, upd_gamma, upd_bias, st) : MOE_OK;
     }
     if (moe::launch_route_rows(c, ra, st, timed ? &ev : nullptr) != hipSuccess) return MOE_ERR_HIP;
 
@@ -254,8 +267,30 @@ int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
     ca.bpm = c.bpm; ca.nsplit = c.nsplit;
     ca.rows_per_wave = moe::scatter_rows_per_wave(p->E, p->k, scat_nw);
     ca.vec_idx = (p->k % 4 == 0 && aligned(out->topk_idx, 16)) ? 1 : 0;
+    const bool fused_step = upd_bias && p->n_micro == 1;
+    ca.upd_bias = fused_step ? upd_bias : nullptr;
+    ca.upd_gamma = upd_gamma;
     if (moe::launch_route_scatter(c, ca, st) != hipSuccess) return MOE_ERR_HIP;
-    return MOE_OK;
+    return (upd_bias && !fused_step) ? bias_step(p, out->counts, upd_gamma, upd_bias, st) : MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_route(const moe_route_params* p, const float* logits, const uint16_t* X,
+              const uint16_t* Wg, const float* select_bias, const moe_route_out* out,
+              void* workspace, size_t workspace_bytes_given, void* stream) {
+    return route_impl(p, logits, X, Wg, select_bias, out, workspace, workspace_bytes_given, stream, nullptr, 0.f);
+}
+
+int moe_route_with_bias_update(const moe_route_params* p, const float* logits, const uint16_t* X,
+                               const uint16_t* Wg, float* select_bias, float gamma, const moe_route_out* out,
+                               void* workspace, size_t workspace_bytes_given, void* stream) {
+    if (!p || !(p->flags & MOE_SELECT_BIAS)) return MOE_ERR_INVALID_ARG;
+    if (!std::isfinite(gamma) || gamma < 0.f) return MOE_ERR_INVALID_ARG;
+    return route_impl(p, logits, X, Wg, select_bias, out, workspace, workspace_bytes_given, stream,
+                      select_bias, gamma);
 }
 
 int moe_route_noalloc(const moe_route_params* p, const float* logits, const uint16_t* X,

@@ -267,6 +267,10 @@ struct ScatterArgs {
     float* cv;
     float* max_over_mean;
     float* extra;
+    // one microbatch only: the selection bias to step from these counts once
+    // the statistics are formed (nullptr: none), and the step
+    float* upd_bias;
+    float upd_gamma;
 };
 
 // One-launch path for small microbatches (route_small.hip): E a power of

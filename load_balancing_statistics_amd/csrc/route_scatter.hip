@@ -281,6 +281,19 @@ route_scatter_kernel(const ScatterArgs a)
     // tot and lofs are reused by the windows only after their first
     // barrier; the row masks' LDS is free until the first window
     if (stats_block) microbatch_statistics<NW, EPT>(a, mb, tot, lofs, psum, reinterpret_cast<double*>(gm), parts);
+    if (a.upd_bias && (parts & 1)) {
+        // one loss-free balancing step from this (only) microbatch's counts,
+        // the rule of the separate update kernel: the bias of an expert
+        // loaded above the mean goes down by gamma, below it up (exact
+        // integer comparison of load*E with T*k)
+        const int64_t Tk = int64_t(a.Tm) * a.k;
+        for (int e = tid; e < E; e += NW * 64) {
+            const int64_t lhs = int64_t(tot[e]) * E;
+            const float bv = a.upd_bias[e];
+            if (lhs > Tk) a.upd_bias[e] = bv - a.upd_gamma;
+            else if (lhs < Tk) a.upd_bias[e] = bv + a.upd_gamma;
+        }
+    }
     if (stats_only) return;
 
     uint64_t* mym = gm + wave * E;

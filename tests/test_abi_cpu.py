@@ -34,7 +34,7 @@ def test_every_declared_symbol_is_exported(lbs):
     assert set(names) == {"moe_route", "moe_route_noalloc", "moe_route_backward", "moe_route_bias_update",
                           "moe_route_capacity", "moe_route_strerror", "moe_route_workspace_size",
                           "moe_gate_backward", "moe_gate_backward_workspace_size", "moe_eplb_plan",
-                          "moe_sinkhorn_plan"}
+                          "moe_sinkhorn_plan", "moe_route_with_bias_update"}
     for n in names:
         assert hasattr(lib, n), n
     out = subprocess.run(["nm", "-D", "--defined-only", lbs._binding.LIB_PATH],
@@ -190,6 +190,20 @@ def test_moe_route_validates_before_launching(lbs):
     pb = lbs.make_params(64, 8, 2, select_bias=True)
     assert call(full, params=pb) == B.MOE_ERR_INVALID_ARG
     assert call(full, params=pb, bias=fake + 2) == B.MOE_ERR_INVALID_ARG
+    # routing with the bias step: the selection-bias flag, a finite gamma >= 0
+    # and a bias pointer are required, and the forward's own checks apply
+    def call_step(params, bias=fake, gamma=0.1, logits=fake, ws=fake):
+        o = B.moe_route_out(*[full.get(n) for n in B._OUT_FIELDS])
+        return lib.moe_route_with_bias_update(ctypes.byref(params), logits, None, None, bias, gamma,
+                                              ctypes.byref(o), ws, 1 << 20, None)
+    assert call_step(p) == B.MOE_ERR_INVALID_ARG                          # no MOE_SELECT_BIAS
+    assert call_step(pb, gamma=-0.1) == B.MOE_ERR_INVALID_ARG
+    assert call_step(pb, gamma=float("inf")) == B.MOE_ERR_INVALID_ARG
+    assert call_step(pb, bias=None) == B.MOE_ERR_INVALID_ARG
+    assert call_step(pb, logits=None) == B.MOE_ERR_INVALID_ARG
+    assert call_step(pb, ws=None) == B.MOE_ERR_WORKSPACE
+    assert lib.moe_route_with_bias_update(None, None, None, None, None, 0.1, None, None, 0,
+                                          None) == B.MOE_ERR_INVALID_ARG
     # bias update
     assert lib.moe_route_bias_update(ctypes.byref(p), None, 0.1, fake, None) == B.MOE_ERR_INVALID_ARG
     assert lib.moe_route_bias_update(ctypes.byref(p), fake, 0.1, None, None) == B.MOE_ERR_INVALID_ARG

@@ -134,3 +134,46 @@ def test_bias_training_loop_balances():
         torch.cuda.synchronize()
         assert_equal(bt.cpu().numpy(), want, "bias after step")
     assert cvs[-1] < cvs[0], cvs
+
+
+# (T, E, k, n_micro): one microbatch with the step inside the scatter (a
+# statistics workgroup; the statistics spread over six row blocks), several
+# microbatches and the one-launch path (the step by the update kernel)
+STEP_SHAPES = [(3000, 256, 8, 1), (30000, 256, 8, 1), (9000, 64, 2, 1), (4000, 300, 4, 2), (2048, 8, 2, 1)]
+
+
+@pytest.mark.parametrize("shape", STEP_SHAPES, ids=lambda s: "T%d_E%d_k%d_m%d" % s)
+def test_route_with_bias_update(shape):
+    """moe_route_with_bias_update gives the bytes of moe_route followed by
+    moe_route_bias_update, its forward matches the oracle on the bias it
+    started from and its bias step matches the oracle's on the counts."""
+    T, E, k, m = shape
+    print(f"case route_with_bias_update T={T} E={E} k={k} m={m}", flush=True)
+    rng = np.random.default_rng(T + E)
+    L = rng.standard_normal((T, E), dtype=np.float32)
+    b0 = (np.round(rng.standard_normal(E) * 4) / 8).astype(np.float32)
+    gamma = 0.0625
+    p = lbs.make_params(T, E, k, n_micro=m, capacity_factor=1.25, alpha=0.01, renorm=True,
+                        save_row_stats=True, inv_perm=True, select_bias=True)
+    dev = torch.device(DEV)
+    Lg = torch.from_numpy(L).to(dev)
+    res = []
+    for fused in (True, False):
+        out = lbs.alloc_outputs(p, device=dev)
+        ws = lbs.alloc_workspace(p, device=dev)
+        bt = torch.from_numpy(b0.copy()).to(dev)
+        if fused:
+            lbs.moe_route_with_bias_update(p, out, ws, bt, gamma, logits=Lg)
+        else:
+            lbs.moe_route(p, out, ws, logits=Lg, select_bias=bt)
+            lbs.moe_route_bias_update(p, out["counts"], gamma, bt)
+        torch.cuda.synchronize()
+        res.append(({key: v.cpu().numpy() for key, v in out.items() if v is not None}, bt.cpu().numpy()))
+    (g, bias_f), (h, bias_s) = res
+    for key in g:
+        assert np.array_equal(g[key].view(np.uint8), h[key].view(np.uint8)), key
+    assert np.array_equal(bias_f.view(np.uint32), bias_s.view(np.uint32)), "bias"
+    compare_forward(g, oracle_forward(p, L, select_bias=b0), p)
+    want = oracle.bias_update(g["counts"], T=T, k=k, gamma=gamma, bias=b0)
+    assert_equal(bias_f, want, "bias after the step")
+    assert not np.array_equal(bias_f, b0)
